@@ -1,0 +1,166 @@
+/*
+ * sa.h -- C ABI of the MI355X (gfx950) sparse flash-attention forward library (libsa_hip.so).
+ *
+ * Three sibling forward paths and their host-side helpers:
+ *   - skip-softmax attention: KV tiles whose scores are negligible under a threshold lambda are
+ *     skipped inside the FlashAttention loop (Model-Optimizer "Skip-Softmax Sparse Attention for
+ *     Diffusion Models" README: introduction and "Threshold Modes");
+ *   - N:M sparse softmax: in every M consecutive keys keep the top-N scores, the rest become -inf
+ *     before the softmax, with dense attention-sink and recent-token windows (Model-Optimizer
+ *     "Attention Sparsity for HuggingFace Models": "N:M Sparse Softmax");
+ *   - proxy-compensated block-sparse attention driven by packed UInt32 exact-block bitmaps, with
+ *     omitted KV blocks represented by a mean-K / summed-V summary and the denominator corrected
+ *     by the token mass of each summary (FlashInfer block-sparse proxy description quoted in the
+ *     TensorRT-LLM "add VisualGen SOL sparse attention" PR: "Description", "Bitmask format");
+ *   - the calibrated threshold lowering a*exp(b*s)/seq_k ("Threshold Modes").
+ *
+ * Conventions shared by every entry point:
+ *   - Ownership: every buffer is allocated by the caller; device buffers are device pointers
+ *     (e.g. from torch), host scalars are passed by value.  The library allocates nothing and keeps
+ *     no state between calls; calls are reentrant.
+ *   - Streams: `stream` is a hipStream_t (NULL = the default stream).  Every kernel is enqueued
+ *     asynchronously on it; nothing synchronises the host.
+ *   - Errors: all argument checks run on the host before any HIP call.  On an error status nothing
+ *     has been enqueued or written.  SA_ERR_HIP reports a failed launch (hipGetLastError).
+ *   - Dtypes: Q, K, V, O and the proxy summaries are bf16 (uint16 bit patterns), fp32 accumulate.
+ *   - Layout: Q/O are [batch, seqlen_q, heads_q, head_dim], K/V are [batch, seqlen_k, heads_kv,
+ *     head_dim], each addressed through three element strides (batch, sequence, head) with a unit
+ *     head_dim stride.  Every (batch, seq, head) row must start 16-byte aligned: base pointers
+ *     16-byte aligned and strides multiples of 8 elements.
+ *   - GQA: query head h reads KV head h / (heads_q / heads_kv).
+ *   - Causal masking is top-left: query i sees keys k <= i (requires seqlen_q == seqlen_k).
+ */
+#ifndef SA_H
+#define SA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_NULL = 1,        /* a required pointer is NULL */
+  SA_ERR_SHAPE = 2,       /* non-positive size, heads_q % heads_kv != 0, causal with Sq != Sk */
+  SA_ERR_UNSUPPORTED = 3, /* head_dim / tile / (n, m) / causal-proxy combination not implemented */
+  SA_ERR_ALIGN = 4,       /* non-16-byte-aligned pointer or stride */
+  SA_ERR_VALUE = 5,       /* bad scalar: lambda, softmax_scale, calibration inputs, sink/recent */
+  SA_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+} sa_status;
+
+/* Human-readable name of a status code (static string). */
+const char* sa_status_str(sa_status status);
+
+/* Shape and layout of one attention call. */
+typedef struct {
+  int32_t batch, heads_q, heads_kv;
+  int32_t seqlen_q, seqlen_k;
+  int32_t head_dim;        /* 64 or 128 */
+  int32_t causal;          /* 0 or 1 */
+  int32_t block_q;         /* query tile (skip, N:M) or query block (proxy) rows: 64 or 128 */
+  int32_t block_k;         /* key tile (skip, N:M: 64) or semantic KV block (proxy: 64 or 128) */
+  float softmax_scale;     /* > 0 and finite, usually 1/sqrt(head_dim) */
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];  /* batch, seq, head (elements) */
+} sa_attn_desc;
+
+/*
+ * Skip-softmax forward (Model-Optimizer skip-softmax README: introduction, "Threshold Modes").
+ *
+ * FlashAttention over key tiles of block_k keys, in ascending order, per query tile of block_q rows.
+ * With t = softmax_scale*log2(e)*q.k and M_j[r] the row maxima of visited tile j, tile j is skipped
+ * -- no exponentials, no V load, no P.V -- when every valid row r of the query tile satisfies
+ *     M_j[r] < fl32(m[r] + L),   L = (float)log2((double)lambda),
+ * where m[r] is the fp32 running max over the tiles kept so far.  A skipped tile leaves the running
+ * max, sum and accumulator untouched.  lambda == 0 never skips (dense attention); any finite
+ * lambda >= 0 is accepted.
+ *
+ *   lambda            finite, >= 0.
+ *   tile_state        optional, uint8 [B, Hq, nQT, nKT] (nQT = ceil(Sq/block_q), nKT =
+ *                     ceil(Sk/block_k)): 0 kept, 1 skipped, 2 not visited (causal).
+ *   head_counters     optional, uint32 [B, Hq, 2] = {visited tiles, skipped tiles}, ADDED to
+ *                     (the caller zeroes them to start a count).
+ *   lse               optional, fp32 [B, Hq, Sq], natural-log log-sum-exp of the scaled logits
+ *                     over the kept keys.
+ *   dbg_tile_rowmax   optional debug export, fp32 [B, Hq, nQT, nKT, block_q]: the M_j[r] the
+ *                     decision used (log2 domain); -inf for unvisited tiles and empty rows.
+ * Supported: head_dim 64/128, block_q 64/128, block_k 64.
+ */
+sa_status sa_skip_softmax_fwd(const sa_attn_desc* desc, const void* q, const void* k,
+                              const void* v, void* o, float lambda, uint8_t* tile_state,
+                              uint32_t* head_counters, float* lse, float* dbg_tile_rowmax,
+                              void* stream);
+
+/*
+ * N:M sparse softmax forward (Model-Optimizer HuggingFace attention sparsity: "N:M Sparse
+ * Softmax").  For every query row and every group of m consecutive keys (groups aligned to key 0,
+ * the last one clipped to Sk), keys ranked below the top n by raw score q.k (ties to the lower
+ * key index) are set to -inf before the softmax, except keys k < dense_sink_tokens and keys with
+ * 0 <= row - k < dense_recent_tokens, which stay dense.  Masked (causal) keys rank last.
+ *
+ *   (n, m)            m == 4 with n in 1..4, or m == 8 with n in 1..8 (n == m is dense).
+ *   dense_sink_tokens, dense_recent_tokens   >= 0.
+ *   lse               optional, fp32 [B, Hq, Sq].
+ *   dbg_keep_bits     optional debug export, uint32 [B, Hq, Sq, ceil(Sk/32)]: bit k&31 of word
+ *                     k>>5 set when key k is kept (LSB first); padding bits 0.
+ *   dbg_scores        optional debug export, fp32 [B, Hq, Sq, Sk]: the raw q.k the ranking used
+ *                     (-inf where causally masked).
+ * Supported: head_dim 64/128, block_q 64/128, block_k 64.
+ */
+sa_status sa_nm_softmax_fwd(const sa_attn_desc* desc, const void* q, const void* k,
+                            const void* v, void* o, int32_t n, int32_t m,
+                            int32_t dense_sink_tokens, int32_t dense_recent_tokens, float* lse,
+                            uint32_t* dbg_keep_bits, float* dbg_scores, void* stream);
+
+/*
+ * Route preparation, the "plan" step of the block-sparse path (FlashInfer proxy description,
+ * "Bitmask format").  nKB = ceil(Sk/block_k), nQB = ceil(Sq/block_q), W = ceil(nKB/32).
+ *
+ *   bitmask     uint32 [B, Hkv, nQB, W] packed exact-block bitmaps, one per (batch, KV head,
+ *               query block); block j is exact when bit j&31 of word j>>5 is set (LSB first);
+ *               bits j >= nKB are padding and are ignored.
+ *   n_exact     int32 [B, Hkv, nQB]: number of exact blocks.
+ *   exact_idx   int32 [B, Hkv, nQB, nKB]: exact block indices in ascending order, -1 after them.
+ *   proxy_keep  uint32 [B, Hkv, nQB, W]: complement of the exact bits over j < nKB (the blocks a
+ *               proxy summary stands for), padding bits 0.
+ * Only the shape fields of desc are used (strides and scale are ignored).
+ */
+sa_status sa_bitmask_route_prep(const sa_attn_desc* desc, const uint32_t* bitmask,
+                                int32_t* n_exact, int32_t* exact_idx, uint32_t* proxy_keep,
+                                void* stream);
+
+/*
+ * Proxy-compensated block-sparse forward, the "run" step (FlashInfer proxy description,
+ * "Description").  For a query in block qb: exact blocks from (n_exact, exact_idx) contribute
+ * their tokens exactly; when use_proxy != 0, every block j with bit j set in proxy_keep contributes
+ * one summary key k_mean[j] with value v_sum[j] and token mass c_j = min(block_k, Sk - j*block_k):
+ *   O = [sum_t e^{s_t} v_t + sum_j e^{s^_j} v_sum_j] / [sum_t e^{s_t} + sum_j c_j e^{s^_j}],
+ *   s = softmax_scale * q.k.   A row with nothing to attend to gets O = 0 and lse = -inf.
+ *
+ *   k_mean, v_sum   bf16 [B, Hkv, nKB, head_dim], contiguous (caller-provided summaries).
+ *   n_exact, exact_idx, proxy_keep   as produced by sa_bitmask_route_prep.
+ *   lse             optional, fp32 [B, Hq, Sq].
+ * Non-causal only (causal -> SA_ERR_UNSUPPORTED).  Supported: head_dim 128 (and 64),
+ * block_q 128 or 64, block_k 64 or 128.
+ */
+sa_status sa_proxy_block_sparse_fwd(const sa_attn_desc* desc, const void* q, const void* k,
+                                    const void* v, const void* k_mean, const void* v_sum,
+                                    const int32_t* n_exact, const int32_t* exact_idx,
+                                    const uint32_t* proxy_keep, int32_t use_proxy, void* o,
+                                    float* lse, void* stream);
+
+/*
+ * Calibrated threshold lowering, host only ("Threshold Modes"): scale_factor = a*exp(b*s) in
+ * double; lambda = scale_factor / seq_k; outputs are optional.  *lambda_out is the float lambda to
+ * pass to sa_skip_softmax_fwd and *log2_lambda_out = (float)log2((double)*lambda_out), the value
+ * the kernel then uses.  Requires a > 0, finite b, 0 <= target_sparsity < 1, seq_k >= 1.
+ */
+sa_status sa_threshold_from_calib(double a, double b, double target_sparsity, int64_t seq_k,
+                                  double* scale_factor_out, float* lambda_out,
+                                  float* log2_lambda_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_H */

@@ -1,0 +1,184 @@
+"""Python binding of libsa_hip.so, the gfx950 sparse flash-attention forward library.
+
+The functions here carry the C ABI's names (``include/sa.h``) and only marshal arguments: tensor
+shapes and strides become an ``sa_attn_desc``, tensors become device pointers, and the current
+torch stream becomes the ``hipStream_t``.  Every step of the computation runs in the HIP kernels of
+``libsa_hip.so``; there is no fallback path.  Importing this package fails if the library has not
+been built (``python -m sparse_attention_flash_amd.build``).
+
+Tensors: Q/O ``[B, Sq, Hq, D]`` and K/V ``[B, Sk, Hkv, D]`` bf16 on the GPU with a unit stride on
+D; optional outputs are preallocated by the caller with the shapes given in ``sa.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_DIR, "libsa_hip.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_attention_flash_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_ALIGN, SA_ERR_VALUE, SA_ERR_HIP = range(7)
+STATUS_NAMES = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_UNSUPPORTED",
+                4: "SA_ERR_ALIGN", 5: "SA_ERR_VALUE", 6: "SA_ERR_HIP"}
+
+
+class sa_attn_desc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32),
+                ("heads_kv", ctypes.c_int32), ("seqlen_q", ctypes.c_int32),
+                ("seqlen_k", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("block_q", ctypes.c_int32),
+                ("block_k", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+                ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_F = ctypes.c_float
+_D = ctypes.c_double
+_DESC = ctypes.POINTER(sa_attn_desc)
+
+_lib.sa_status_str.argtypes = [ctypes.c_int]
+_lib.sa_status_str.restype = ctypes.c_char_p
+_lib.sa_skip_softmax_fwd.argtypes = [_DESC, _P, _P, _P, _P, _F, _P, _P, _P, _P, _P]
+_lib.sa_skip_softmax_fwd.restype = ctypes.c_int
+_lib.sa_nm_softmax_fwd.argtypes = [_DESC, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P]
+_lib.sa_nm_softmax_fwd.restype = ctypes.c_int
+_lib.sa_bitmask_route_prep.argtypes = [_DESC, _P, _P, _P, _P, _P]
+_lib.sa_bitmask_route_prep.restype = ctypes.c_int
+_lib.sa_proxy_block_sparse_fwd.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P]
+_lib.sa_proxy_block_sparse_fwd.restype = ctypes.c_int
+_lib.sa_threshold_from_calib.argtypes = [_D, _D, _D, ctypes.c_int64, _P, _P, _P]
+_lib.sa_threshold_from_calib.restype = ctypes.c_int
+
+raw = _lib   # the ctypes handle, for callers that pass raw pointers
+
+
+class SaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {sa_status_str(status)}")
+
+
+def sa_status_str(status: int) -> str:
+    return _lib.sa_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != SA_OK:
+        raise SaError(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _bsh_strides(t, name):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [batch, seq, heads, head_dim]")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name} needs a unit stride on head_dim")
+    return (t.stride(0), t.stride(1), t.stride(2))
+
+
+def make_desc(q, k, v=None, o=None, *, causal=False, block_q=128, block_k=64, scale=None):
+    """sa_attn_desc from tensor shapes/strides (v and o default to the strides of k and q)."""
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    d = sa_attn_desc()
+    d.batch, d.heads_q, d.heads_kv, d.seqlen_q, d.seqlen_k, d.head_dim = B, Hq, Hkv, Sq, Sk, D
+    d.causal = int(bool(causal))
+    d.block_q, d.block_k = int(block_q), int(block_k)
+    d.softmax_scale = float(scale) if scale is not None else 1.0 / math.sqrt(D)
+    qs = _bsh_strides(q, "q")
+    ks = _bsh_strides(k, "k")
+    vs = _bsh_strides(v, "v") if v is not None else ks
+    os_ = _bsh_strides(o, "o") if o is not None else qs
+    for i in range(3):
+        d.q_stride[i], d.k_stride[i], d.v_stride[i], d.o_stride[i] = qs[i], ks[i], vs[i], os_[i]
+    return d
+
+
+def sa_skip_softmax_fwd(q, k, v, o, lam, *, causal=False, block_q=128, block_k=64, scale=None,
+                        tile_state=None, head_counters=None, lse=None, dbg_tile_rowmax=None,
+                        stream=None):
+    d = make_desc(q, k, v, o, causal=causal, block_q=block_q, block_k=block_k, scale=scale)
+    _check(_lib.sa_skip_softmax_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                    float(lam), _ptr(tile_state), _ptr(head_counters), _ptr(lse),
+                                    _ptr(dbg_tile_rowmax), _stream(stream)),
+           "sa_skip_softmax_fwd")
+
+
+def sa_nm_softmax_fwd(q, k, v, o, n, m, dense_sink_tokens=0, dense_recent_tokens=0, *,
+                      causal=False, block_q=128, block_k=64, scale=None, lse=None,
+                      dbg_keep_bits=None, dbg_scores=None, stream=None):
+    d = make_desc(q, k, v, o, causal=causal, block_q=block_q, block_k=block_k, scale=scale)
+    _check(_lib.sa_nm_softmax_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), int(n),
+                                  int(m), int(dense_sink_tokens), int(dense_recent_tokens),
+                                  _ptr(lse), _ptr(dbg_keep_bits), _ptr(dbg_scores),
+                                  _stream(stream)),
+           "sa_nm_softmax_fwd")
+
+
+def sa_bitmask_route_prep(bitmask, n_exact, exact_idx, proxy_keep, *, batch, heads_kv, seqlen_q,
+                          seqlen_k, block_q, block_k, stream=None):
+    d = sa_attn_desc()
+    d.batch, d.heads_kv, d.heads_q = batch, heads_kv, heads_kv
+    d.seqlen_q, d.seqlen_k, d.block_q, d.block_k = seqlen_q, seqlen_k, block_q, block_k
+    for t, dt in ((bitmask, torch.int32), (n_exact, torch.int32), (exact_idx, torch.int32),
+                  (proxy_keep, torch.int32)):
+        if t.dtype not in (torch.int32, torch.uint32) or not t.is_contiguous():
+            raise TypeError("route tensors must be contiguous 32-bit integer tensors")
+    _check(_lib.sa_bitmask_route_prep(ctypes.byref(d), _ptr(bitmask), _ptr(n_exact),
+                                      _ptr(exact_idx), _ptr(proxy_keep), _stream(stream)),
+           "sa_bitmask_route_prep")
+
+
+def sa_proxy_block_sparse_fwd(q, k, v, k_mean, v_sum, n_exact, exact_idx, proxy_keep, use_proxy,
+                              o, *, block_q=128, block_k=128, scale=None, lse=None, stream=None):
+    d = make_desc(q, k, v, o, causal=False, block_q=block_q, block_k=block_k, scale=scale)
+    for t in (k_mean, v_sum):
+        if t is not None and (t.dtype != torch.bfloat16 or not t.is_contiguous()):
+            raise TypeError("k_mean / v_sum must be contiguous bfloat16 [B, Hkv, nKB, D]")
+    _check(_lib.sa_proxy_block_sparse_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(k_mean), _ptr(v_sum), _ptr(n_exact),
+                                          _ptr(exact_idx), _ptr(proxy_keep), int(use_proxy),
+                                          _ptr(o), _ptr(lse), _stream(stream)),
+           "sa_proxy_block_sparse_fwd")
+
+
+def sa_threshold_from_calib(a, b, target_sparsity, seq_k):
+    """(scale_factor, lambda, log2_lambda) with lambda and log2_lambda as the kernel sees them."""
+    sf, lam, l2 = ctypes.c_double(), ctypes.c_float(), ctypes.c_float()
+    _check(_lib.sa_threshold_from_calib(float(a), float(b), float(target_sparsity), int(seq_k),
+                                        ctypes.addressof(sf), ctypes.addressof(lam),
+                                        ctypes.addressof(l2)),
+           "sa_threshold_from_calib")
+    return sf.value, lam.value, l2.value
+
+
+def tile_counts(seqlen_q, seqlen_k, block_q, block_k):
+    """(nQT, nKT) tile counts for a call."""
+    return -(-seqlen_q // block_q), -(-seqlen_k // block_k)

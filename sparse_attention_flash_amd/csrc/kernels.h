@@ -1,0 +1,63 @@
+// kernels.h -- internal launch interface between the C-ABI host layer and the gfx950 kernels.
+// Host code fills these plain structs after validating the call; launchers enqueue on `stream`
+// and return the hipGetLastError() status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+struct AttnGeom {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t qs[3], ks[3], vs[3], os[3];   // batch, seq, head strides (elements)
+  int B, Hq, Hkv, Sq, Sk, D, causal, block_q, block_k;
+  float c32;                            // softmax_scale * log2(e), rounded to fp32
+};
+
+struct SkipArgs {
+  AttnGeom g;
+  float L32;                            // log2(lambda) in fp32; -inf when lambda == 0
+  uint8_t* tile_state;
+  uint32_t* counters;
+  float* lse;
+  float* rowmax;
+};
+
+struct NmArgs {
+  AttnGeom g;
+  int n, m, sink, recent;
+  float* lse;
+  uint32_t* keep_bits;
+  float* scores;
+};
+
+struct RouteArgs {
+  const uint32_t* bitmask;
+  int32_t* n_exact;
+  int32_t* exact_idx;
+  uint32_t* proxy_keep;
+  int64_t rows;                         // B * Hkv * nQB
+  int nKB, W;
+};
+
+struct ProxyArgs {
+  AttnGeom g;
+  const void* k_mean;
+  const void* v_sum;
+  const int32_t* n_exact;
+  const int32_t* exact_idx;
+  const uint32_t* proxy_keep;
+  int use_proxy;
+  float* lse;
+};
+
+hipError_t launch_skip_softmax(const SkipArgs& a, hipStream_t stream);
+hipError_t launch_nm_softmax(const NmArgs& a, hipStream_t stream);
+hipError_t launch_route_prep(const RouteArgs& a, hipStream_t stream);
+hipError_t launch_proxy(const ProxyArgs& a, hipStream_t stream);
+
+}  // namespace sa

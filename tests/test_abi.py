@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point sa.h declares, and
+rejects every invalid call on the host before any HIP call (all calls here are invalid, so no
+kernel is ever launched; the pointers are dummies)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+sa = pytest.importorskip("sparse_attention_flash_amd")
+
+FAKE = 0x10000          # 16-byte aligned dummy address, never dereferenced
+FAKE_MIS = 0x10008      # misaligned dummy address
+
+
+def declared_entry_points():
+    text = open(os.path.join(ROOT, "include", "sa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_entry_points()
+    assert {"sa_skip_softmax_fwd", "sa_nm_softmax_fwd", "sa_bitmask_route_prep",
+            "sa_proxy_block_sparse_fwd", "sa_threshold_from_calib", "sa_status_str"} <= set(names)
+    lib = ctypes.CDLL(sa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in range(7):
+        assert sa.sa_status_str(code).startswith(sa.STATUS_NAMES[code])
+
+
+def _desc(**kw):
+    d = sa.sa_attn_desc()
+    base = dict(batch=1, heads_q=4, heads_kv=2, seqlen_q=256, seqlen_k=256, head_dim=128,
+                causal=0, block_q=128, block_k=64, softmax_scale=1 / math.sqrt(128))
+    base.update({k: v for k, v in kw.items() if not k.endswith("stride")})
+    for k, v in base.items():
+        setattr(d, k, v)
+    for name in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        default = (256 * 4 * 128, 4 * 128, 128) if name[0] in "qo" else (256 * 2 * 128, 256, 128)
+        s = kw.get(name, default)
+        for i in range(3):
+            getattr(d, name)[i] = s[i]
+    return d
+
+
+def _skip(d, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lam=0.1):
+    return sa.raw.sa_skip_softmax_fwd(ctypes.byref(d), q, k, v, o, lam, None, None, None, None, None)
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(batch=0), sa.SA_ERR_SHAPE),
+    (dict(seqlen_k=0), sa.SA_ERR_SHAPE),
+    (dict(heads_q=3), sa.SA_ERR_SHAPE),
+    (dict(causal=1, seqlen_q=128), sa.SA_ERR_SHAPE),
+    (dict(causal=2), sa.SA_ERR_VALUE),
+    (dict(head_dim=96), sa.SA_ERR_UNSUPPORTED),
+    (dict(block_q=32), sa.SA_ERR_UNSUPPORTED),
+    (dict(block_k=128), sa.SA_ERR_UNSUPPORTED),
+    (dict(softmax_scale=0.0), sa.SA_ERR_VALUE),
+    (dict(softmax_scale=float("nan")), sa.SA_ERR_VALUE),
+    (dict(q_stride=(256 * 4 * 128, 4 * 128, 4)), sa.SA_ERR_ALIGN),
+    (dict(k_stride=(-256, 256, 128)), sa.SA_ERR_ALIGN),
+])
+def test_skip_rejects_bad_desc(change, code):
+    assert _skip(_desc(**change)) == code
+
+
+@pytest.mark.parametrize("lam", [-1.0, float("nan"), float("inf")])
+def test_skip_rejects_bad_lambda(lam):
+    assert _skip(_desc(), lam=lam) == sa.SA_ERR_VALUE
+
+
+def test_skip_rejects_null_and_misaligned():
+    assert _skip(_desc(), q=None) == sa.SA_ERR_NULL
+    assert sa.raw.sa_skip_softmax_fwd(None, FAKE, FAKE, FAKE, FAKE, 0.1, None, None, None, None,
+                                      None) == sa.SA_ERR_NULL
+    assert _skip(_desc(), v=FAKE_MIS) == sa.SA_ERR_ALIGN
+
+
+@pytest.mark.parametrize("n,m,sink,recent,code", [
+    (0, 4, 0, 0, sa.SA_ERR_UNSUPPORTED), (5, 4, 0, 0, sa.SA_ERR_UNSUPPORTED),
+    (2, 6, 0, 0, sa.SA_ERR_UNSUPPORTED), (9, 8, 0, 0, sa.SA_ERR_UNSUPPORTED),
+    (2, 4, -1, 0, sa.SA_ERR_VALUE), (2, 4, 0, -5, sa.SA_ERR_VALUE),
+])
+def test_nm_rejects(n, m, sink, recent, code):
+    d = _desc(causal=1)
+    assert sa.raw.sa_nm_softmax_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, n, m, sink, recent,
+                                    None, None, None, None) == code
+
+
+def test_route_prep_rejects():
+    d = _desc(block_k=128)
+    assert sa.raw.sa_bitmask_route_prep(ctypes.byref(d), None, FAKE, FAKE, FAKE, None) == sa.SA_ERR_NULL
+    assert sa.raw.sa_bitmask_route_prep(None, FAKE, FAKE, FAKE, FAKE, None) == sa.SA_ERR_NULL
+    d0 = _desc(block_k=0)
+    assert sa.raw.sa_bitmask_route_prep(ctypes.byref(d0), FAKE, FAKE, FAKE, FAKE, None) == sa.SA_ERR_SHAPE
+
+
+def _proxy(d, use_proxy=1, km=FAKE, vs=FAKE, routes=FAKE):
+    return sa.raw.sa_proxy_block_sparse_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, km, vs, routes,
+                                            FAKE, FAKE, use_proxy, FAKE, None, None)
+
+
+def test_proxy_rejects():
+    assert _proxy(_desc(block_k=128, causal=1)) == sa.SA_ERR_UNSUPPORTED
+    assert _proxy(_desc(block_k=32)) == sa.SA_ERR_UNSUPPORTED
+    assert _proxy(_desc(block_k=128), km=None) == sa.SA_ERR_NULL
+    assert _proxy(_desc(block_k=128), routes=None) == sa.SA_ERR_NULL
+    assert _proxy(_desc(block_k=128), vs=FAKE_MIS) == sa.SA_ERR_ALIGN
+
+
+def test_threshold_matches_oracle_and_rejects():
+    for s in (0.0, 0.5, 0.7, 0.95):
+        for seq_k in (256, 8192, 16257, 32760):
+            sf, lam, l2 = sa.sa_threshold_from_calib(1443.49, 4.30, s, seq_k)
+            osf, olam, ol2 = oracle.threshold(1443.49, 4.30, s, seq_k)
+            assert sf == pytest.approx(osf, rel=1e-15)
+            assert lam == pytest.approx(olam, rel=6e-8)       # float32 rounding of lambda
+            assert l2 == pytest.approx(math.log2(lam), abs=1e-6)
+    for args in [(0.0, 4.3, 0.5, 10), (1443.49, float("nan"), 0.5, 10), (1443.49, 4.3, 1.0, 10),
+                 (1443.49, 4.3, -0.1, 10), (1443.49, 4.3, 0.5, 0)]:
+        with pytest.raises(sa.SaError) as e:
+            sa.sa_threshold_from_calib(*args)
+        assert e.value.status == sa.SA_ERR_VALUE
