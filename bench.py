@@ -1,0 +1,365 @@
+#!/usr/bin/env python
+"""Benchmark of the sparse flash-attention forward library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-paths]
+
+One step is one pass of the skip-softmax hot path over the headline workload: the calibrated
+threshold lowering (host, a*exp(b*0.5)/seq_k) followed by the skip-softmax forward with its tile
+state and per-head counters, on the video-DiT self-attention shape (batch 1, 40 heads, 32760
+tokens = 21x30x52, head_dim 128, non-causal, 128x64 tiles), inputs seeded and synthetic and
+resident in HBM before timing.  W untimed steps, then exactly K steps between two
+torch.cuda.synchronize() calls, timed with HIP events on the launch stream.  Afterwards (untimed
+for the headline) the same kernel at lambda = 0, and the sibling paths at their own workloads,
+are timed the same way and reported under "paths".
+
+Prints ONE JSON line.  value = computed TFLOP/s of the skip-softmax kernel (QK^T flops of every
+visited tile + P.V flops of every kept tile, unmasked pairs only); dense_equiv_tflops counts the
+full attention's flops over the same time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (no sparsity)
+HEADLINE = "video_dit_s32760"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-paths", action="store_true", help="only the headline workload")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target wall time of the CPU-oracle sample")
+    p.add_argument("--profile", action="store_true",
+                   help="headline kernel only (no lambda=0 arm, no paths, no CPU baseline), for "
+                        "profiler runs: dispatches = warmup + steps launches of one kernel")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                   help="only run 5 device-to-device copies of BYTES bytes (a plain copy kernel "
+                        "of known size, used to scale the HBM byte counters) and exit")
+    return p.parse_args()
+
+
+def copy_probe(nbytes):
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "dispatches": 5}))
+
+
+# ------------------------------------------------------------------------------------------------
+# algorithmic work
+# ------------------------------------------------------------------------------------------------
+def tile_pairs(Sq, Sk, Br, Bc, causal):
+    """Unmasked (query, key) pairs of every (query tile, key tile): int64 [nQT, nKT]."""
+    nQT, nKT = -(-Sq // Br), -(-Sk // Bc)
+    P = np.zeros((nQT, nKT), np.int64)
+    for i in range(nQT):
+        r0, r1 = i * Br, min(Sq, (i + 1) * Br)
+        for j in range(nKT):
+            k0, k1 = j * Bc, min(Sk, (j + 1) * Bc)
+            if not causal:
+                P[i, j] = (r1 - r0) * (k1 - k0)
+            else:
+                # sum over rows r of #keys k in [k0, k1) with k <= r
+                rows = np.arange(r0, r1)
+                P[i, j] = np.clip(np.minimum(rows + 1, k1) - k0, 0, None).sum()
+    return P
+
+
+def skip_flops(tile_state, P, D):
+    """(computed, dense-equivalent) flops: QK on visited tiles + PV on kept tiles, unmasked."""
+    st = tile_state.reshape(-1, *P.shape)
+    visited = (st != 2)
+    kept = (st == 0)
+    computed = 2 * D * (P[None] * visited).sum() + 2 * D * (P[None] * kept).sum()
+    dense = 4 * D * P.sum() * st.shape[0]
+    return int(computed), int(dense)
+
+
+# ------------------------------------------------------------------------------------------------
+# timing
+# ------------------------------------------------------------------------------------------------
+def time_steps(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+SKIP_SOURCES = ["sparse_attention_flash_amd/csrc/skip_softmax.hip",
+                "sparse_attention_flash_amd/csrc/tile_core.h"]
+
+
+def measured_traffic(kernel_key, per_launch_algorithmic):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel source (else None)."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel_key)
+    if not rec or rec.get("source_digest") != source_digest(SKIP_SOURCES):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the headline workload
+# ------------------------------------------------------------------------------------------------
+def cpu_baseline(q, k, v, wl, lam, P, target_s):
+    import oracle
+    B, S, H, D = q.shape
+    nQT = P.shape[0]
+    rng = np.random.default_rng(0)
+    units = rng.permutation(B * H * nQT)
+    threads = oracle.num_threads()
+    done, flops, t0 = 0, 0, time.perf_counter()
+    batch = max(1, threads)
+    while done < units.size:
+        sel = units[done:done + batch]
+        _, _, st, _ = oracle.skip_softmax(q, k, v, causal=wl.causal, block_q=wl.block_q,
+                                          block_k=wl.block_k, scale=wl.scale, lam=lam, units=sel)
+        qt = sel % nQT
+        Pu = P[qt]
+        flops += int(2 * D * (Pu * (st != 2)).sum() + 2 * D * (Pu * (st == 0)).sum())
+        done += sel.size
+        if time.perf_counter() - t0 >= target_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} of {units.size} query tiles (seeded random order) of the "
+                      f"{wl.name} workload at the same lambda, float64 oracle, {el:.1f} s"}
+
+
+# ------------------------------------------------------------------------------------------------
+# sibling paths, each at its own workload (reported beside the headline)
+# ------------------------------------------------------------------------------------------------
+def run_paths(torch, sa, W, to_dev, steps, warmup):
+    out = {}
+    dev = torch.device("cuda:0")
+
+    # causal GQA LLM prefill, skip-softmax at the calibrated lambda and at lambda = 0
+    wl = W.WORKLOADS["llm_prefill_gqa_s8192"]
+    q, k, v = wl.generate()
+    B, S, Hq, D = q.shape
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o = torch.empty_like(qd)
+    nQT, nKT = -(-S // wl.block_q), -(-S // wl.block_k)
+    st = torch.empty((B, Hq, nQT, nKT), dtype=torch.uint8, device=dev)
+    _, lam, _ = sa.sa_threshold_from_calib(W.CALIB_A, W.CALIB_B, wl.param("target_sparsity"), S)
+    P = tile_pairs(S, S, wl.block_q, wl.block_k, True)
+    rec = {"lambda": lam}
+    for name, lm in (("calibrated", lam), ("lambda0", 0.0)):
+        ms = time_steps(torch, lambda: sa.sa_skip_softmax_fwd(
+            qd, kd, vd, o, lm, causal=True, block_q=wl.block_q, block_k=wl.block_k,
+            tile_state=st), steps, warmup)
+        ts = st.cpu().numpy()
+        comp, dense = skip_flops(ts, P, D)
+        rec[name] = {"ms": round(ms, 4), "computed_tflops": round(comp / ms / 1e9, 2),
+                     "dense_equiv_tflops": round(dense / ms / 1e9, 2),
+                     "tile_sparsity": round(float((ts == 1).sum() / max(1, (ts != 2).sum())), 4)}
+    rec["speedup_vs_lambda0"] = round(rec["lambda0"]["ms"] / rec["calibrated"]["ms"], 3)
+    out[wl.name] = rec
+    del qd, kd, vd, o, st
+
+    # causal N:M sparse softmax (no flop saving by design: report dense-equivalent throughput)
+    wl = W.WORKLOADS["llm_prefill_nm_s4096"]
+    q, k, v = wl.generate()
+    B, S, H, D = q.shape
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o = torch.empty_like(qd)
+    dense = 4 * D * tile_pairs(S, S, wl.block_q, wl.block_k, True).sum() * B * H
+    rec = {}
+    try:
+        for n, m in ((2, 4), (4, 4), (1, 4), (3, 4), (1, 8), (4, 8), (7, 8)):
+            ms = time_steps(torch, lambda: sa.sa_nm_softmax_fwd(
+                qd, kd, vd, o, n, m, wl.param("sink"), wl.param("recent"), causal=True,
+                block_q=wl.block_q, block_k=wl.block_k), steps, warmup)
+            rec[f"{n}:{m}"] = {"ms": round(ms, 4), "dense_equiv_tflops": round(dense / ms / 1e9, 2)}
+        rec["overhead_2:4_vs_4:4"] = round(rec["2:4"]["ms"] / rec["4:4"]["ms"] - 1, 4)
+    except sa.SaError as e:
+        rec = {"unavailable": str(e)}
+    out[wl.name] = rec
+    del qd, kd, vd, o
+
+    # proxy-compensated block-sparse attention with bitmask routes
+    wl = W.WORKLOADS["proxy_bitmask_s16257"]
+    q, k, v = wl.generate()
+    B, S, H, D = q.shape
+    Bq, Bk = wl.block_q, wl.block_k
+    nQB, nKB = -(-S // Bq), -(-S // Bk)
+    n_set = int(round(wl.param("density") * nKB))
+    bm = W.gen_bitmask(wl.seed, B, H, nQB, nKB, n_set)
+    km, vs = W.block_summaries(k, v, Bk)
+    qd, kd, vd, kmd, vsd = to_dev(q), to_dev(k), to_dev(v), to_dev(km), to_dev(vs)
+    o = torch.empty_like(qd)
+    bmd = torch.from_numpy(bm.view(np.int32)).to(dev)
+    n_exact = torch.empty((B, H, nQB), dtype=torch.int32, device=dev)
+    idx = torch.empty((B, H, nQB, nKB), dtype=torch.int32, device=dev)
+    keep = torch.empty_like(bmd)
+    rec = {"exact_blocks_per_row": n_set, "n_kv_blocks": nKB}
+    try:
+        def prep():
+            sa.sa_bitmask_route_prep(bmd, n_exact, idx, keep, batch=B, heads_kv=H, seqlen_q=S,
+                                     seqlen_k=S, block_q=Bq, block_k=Bk)
+        rec["route_prep_ms"] = round(time_steps(torch, prep, steps, warmup), 5)
+        ne = n_exact.cpu().numpy().astype(np.int64)
+        # exact work: every query row against the tokens of its exact blocks
+        lens = np.minimum(Bk, S - np.arange(nKB) * Bk)
+        rows = np.minimum(Bq, S - np.arange(nQB) * Bq)
+        ix = idx.cpu().numpy()
+        exact_tokens = np.where(ix >= 0, lens[np.clip(ix, 0, None)], 0).sum(-1)   # [B,H,nQB]
+        exact_flops = int(4 * D * (exact_tokens * rows[None, None]).sum())
+        proxy_flops = int(4 * D * ((nKB - ne) * rows[None, None]).sum())
+        for name, use in (("proxy_off", 0), ("proxy_on", 1)):
+            ms = time_steps(torch, lambda: sa.sa_proxy_block_sparse_fwd(
+                qd, kd, vd, kmd, vsd, n_exact, idx, keep, use, o, block_q=Bq, block_k=Bk),
+                steps, warmup)
+            fl = exact_flops + (proxy_flops if use else 0)
+            rec[name] = {"ms": round(ms, 4), "computed_tflops": round(fl / ms / 1e9, 2)}
+        rec["proxy_overhead"] = round(rec["proxy_on"]["ms"] / rec["proxy_off"]["ms"] - 1, 4)
+    except sa.SaError as e:
+        rec["unavailable"] = str(e)
+    out[wl.name] = rec
+    return out
+
+
+# ------------------------------------------------------------------------------------------------
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the kernels are "
+              "single-GPU and no multi-GPU path is part of this library", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+    if args.profile:
+        args.no_paths = args.no_cpu_baseline = True
+
+    import torch
+    import sparse_attention_flash_amd as sa
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+
+    wl = W.WORKLOADS[HEADLINE]
+    t_gen = time.perf_counter()
+    q, k, v = wl.generate()
+    t_gen = time.perf_counter() - t_gen
+    B, S, H, D = q.shape
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o = torch.empty_like(qd)
+    Br, Bc = wl.block_q, wl.block_k
+    nQT, nKT = -(-S // Br), -(-S // Bc)
+    st = torch.empty((B, H, nQT, nKT), dtype=torch.uint8, device=dev)
+    cnt = torch.zeros((B, H, 2), dtype=torch.int32, device=dev)
+    target = wl.param("target_sparsity")
+    calls = [0]
+
+    def step():
+        _, lam_k, _ = sa.sa_threshold_from_calib(W.CALIB_A, W.CALIB_B, target, S)
+        sa.sa_skip_softmax_fwd(qd, kd, vd, o, lam_k, causal=wl.causal, block_q=Br, block_k=Bc,
+                               tile_state=st, head_counters=cnt)
+        calls[0] += 1
+
+    ms = time_steps(torch, step, args.steps, args.warmup)
+    _, lam, log2_lam = sa.sa_threshold_from_calib(W.CALIB_A, W.CALIB_B, target, S)
+    P = tile_pairs(S, S, Br, Bc, wl.causal)
+    tile_state = st.cpu().numpy()
+    computed, dense = skip_flops(tile_state, P, D)
+    counters = cnt.cpu().numpy().astype(np.int64)
+    visited, skipped = counters[..., 0].sum() // calls[0], counters[..., 1].sum() // calls[0]
+    sparsity = skipped / max(1, visited)
+    tflops = computed / (ms * 1e-3) / 1e12
+
+    # the same kernel and build at lambda = 0 (dense baseline)
+    def step0():
+        sa.sa_skip_softmax_fwd(qd, kd, vd, o, 0.0, causal=wl.causal, block_q=Br, block_k=Bc,
+                               tile_state=st, head_counters=cnt)
+
+    ms0 = float("nan") if args.profile else time_steps(torch, step0, args.steps, args.warmup)
+    computed0, _ = skip_flops(np.zeros_like(tile_state), P, D)
+
+    result = {
+        "metric": "attention TFLOP/s (computed + dense-equiv) & % bf16 MFMA peak at 50% sparsity",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded video-DiT-like Q/K/V with 3-D Gaussian locality bias; "
+                "no dataset or weights)",
+        "config": {"workload": HEADLINE, "batch": B, "heads": H, "seq_len": S, "head_dim": D,
+                   "causal": wl.causal, "tile": f"{Br}x{Bc}", "target_sparsity": target,
+                   "lambda": lam, "log2_lambda": log2_lam},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("skip_softmax_video_dit_s32760", computed)},
+        "dense_equiv_tflops": round(dense / (ms * 1e-3) / 1e12, 2),
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "tile_sparsity": round(float(sparsity), 4),
+        "lambda0_ms": None if args.profile else round(ms0, 4),
+        "lambda0_tflops": None if args.profile else round(computed0 / (ms0 * 1e-3) / 1e12, 2),
+        "speedup_vs_lambda0": None if args.profile else round(ms0 / ms, 3),
+        "computed_flops_per_step": computed,
+        "dense_flops_per_step": dense,
+        "input_generation_s": round(t_gen, 1),
+        "timing": "hipEvent over the timed steps on the launch stream; L2/MALL not flushed "
+                  "between steps",
+    }
+    if not args.no_paths:
+        del qd, kd, vd, o
+        torch.cuda.empty_cache()
+        result["paths"] = run_paths(torch, sa, W, to_dev, args.steps, args.warmup)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(q, k, v, wl, lam, P, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

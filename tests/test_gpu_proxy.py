@@ -1,0 +1,103 @@
+"""GPU parity of sa_bitmask_route_prep (bit-exact) and sa_proxy_block_sparse_fwd (max-abs 2e-2,
+mean-abs 2e-3 against the float64 oracle), needs an MI355X."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import announce, assert_output_parity, err, from_dev_bf16, to_dev
+
+pytestmark = pytest.mark.gpu
+
+sa = pytest.importorskip("sparse_attention_flash_amd")
+
+
+def i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).to("cuda")
+
+
+def route_gpu(bm, B, Hkv, Sq, Sk, Bq, Bk):
+    nQB, nKB = -(-Sq // Bq), -(-Sk // Bk)
+    Wd = -(-nKB // 32)
+    bmd = i32(bm)
+    n_exact = torch.full((B, Hkv, nQB), -7, dtype=torch.int32, device="cuda")
+    idx = torch.full((B, Hkv, nQB, nKB), -7, dtype=torch.int32, device="cuda")
+    keep = torch.full((B, Hkv, nQB, Wd), -7, dtype=torch.int32, device="cuda")
+    sa.sa_bitmask_route_prep(bmd, n_exact, idx, keep, batch=B, heads_kv=Hkv, seqlen_q=Sq,
+                             seqlen_k=Sk, block_q=Bq, block_k=Bk)
+    return n_exact, idx, keep
+
+
+@pytest.mark.parametrize("S,Bk", [(64, 64), (257, 64), (16257, 128), (16257, 64), (32760, 64),
+                                  (300000, 64)])
+def test_route_prep_bit_exact(S, Bk):
+    announce(f"route prep S={S} Bk={Bk}")
+    B, Hkv, Bq = 2, 3, 128
+    nQB, nKB = -(-S // Bq), -(-S // Bk)
+    nQB = min(nQB, 40)          # rows are independent; a prefix of query blocks suffices
+    Sq = nQB * Bq
+    bm = W.gen_bitmask(51, B, Hkv, nQB, nKB, max(1, nKB // 4), garbage_padding=True)
+    ne, ix, kp = route_gpu(bm, B, Hkv, Sq, S, Bq, Bk)
+    torch.cuda.synchronize()
+    r_ne, r_ix, r_kp = oracle.route_prep(bm, nKB)
+    assert np.array_equal(ne.cpu().numpy(), r_ne)
+    assert np.array_equal(ix.cpu().numpy(), r_ix)
+    assert np.array_equal(kp.cpu().numpy().view(np.uint32), r_kp)
+
+
+def run_proxy(q, k, v, bm, Bq, Bk, use_proxy):
+    B, S, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    km, vs = W.block_summaries(k, v, Bk)
+    ne, ix, kp = route_gpu(bm, B, Hkv, S, Sk, Bq, Bk)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o = torch.full((B, S, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, Hq, S), float("nan"), device="cuda")
+    sa.sa_proxy_block_sparse_fwd(qd, kd, vd, to_dev(km), to_dev(vs), ne, ix, kp, use_proxy, o,
+                                 block_q=Bq, block_k=Bk, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.proxy_fwd(q, k, v, km, vs, bm, block_q=Bq, block_k=Bk,
+                                      scale=1 / math.sqrt(D), use_proxy=use_proxy)
+    return from_dev_bf16(o), lse.cpu().numpy(), o_ref, lse_ref
+
+
+@pytest.mark.parametrize("use_proxy", [0, 1])
+@pytest.mark.parametrize("cfg", [
+    # (B, S, Hq, Hkv, D, Bq, Bk, density)
+    (1, 256, 2, 2, 128, 128, 128, 0.5),
+    (1, 257, 2, 1, 128, 128, 128, 0.5),     # 1-token final block, GQA
+    (1, 257, 2, 2, 128, 64, 64, 0.4),
+    (2, 1000, 2, 2, 64, 128, 64, 0.25),
+    (1, 2049, 4, 2, 128, 128, 128, 0.25),
+])
+def test_proxy_parity(cfg, use_proxy):
+    B, S, Hq, Hkv, D, Bq, Bk, dens = cfg
+    announce(f"proxy {cfg} use_proxy={use_proxy}")
+    q, k, v = W.gen_iid(52, B, S, S, Hq, Hkv, D)
+    nQB, nKB = -(-S // Bq), -(-S // Bk)
+    bm = W.gen_bitmask(52, B, Hkv, nQB, nKB, max(1, int(round(dens * nKB))), garbage_padding=True)
+    o, lse, o_ref, lse_ref = run_proxy(q, k, v, bm, Bq, Bk, use_proxy)
+    assert_output_parity(o, o_ref, f"proxy {cfg}")
+    lmx, _ = err(lse, lse_ref)
+    assert lmx < 2e-3
+
+
+def test_all_ones_is_dense_and_empty_rows_are_zero():
+    announce("proxy all-ones / empty")
+    B, S, H, D, Bq, Bk = 1, 300, 2, 128, 128, 64
+    q, k, v = W.gen_iid(53, B, S, S, H, H, D)
+    nQB, nKB = -(-S // Bq), -(-S // Bk)
+    ones = np.full((B, H, nQB, 1), 0xFFFFFFFF, np.uint32)
+    o1, _, _, _ = run_proxy(q, k, v, ones, Bq, Bk, 1)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    od = torch.empty_like(qd)
+    sa.sa_skip_softmax_fwd(qd, kd, vd, od, 0.0, causal=False, block_q=128)
+    torch.cuda.synchronize()
+    assert err(o1, from_dev_bf16(od))[0] <= 1e-2
+    empty = np.zeros((B, H, nQB, 1), np.uint32)
+    empty[:, :, 1:] = 1
+    o0, lse0, _, _ = run_proxy(q, k, v, empty, Bq, Bk, 0)
+    assert (o0[:, :Bq] == 0).all() and np.isneginf(lse0[:, :, :Bq]).all()

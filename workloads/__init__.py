@@ -31,6 +31,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
 
 import numpy as np
 
@@ -118,27 +119,39 @@ def video_positions(frames, rows, cols):
     return np.stack([f.ravel(), r.ravel(), c.ravel()], axis=1).astype(np.float64)
 
 
-def gen_video(seed, B, H, D, grid=(21, 30, 52), sigma=(2.0, 4.0, 4.0), rank=64):
-    """Video-DiT-like Q/K/V on a (frames, rows, cols) token grid; S = prod(grid)."""
+def _video_head(seed, b, h, D, pos, sigma, rank):
+    S = pos.shape[0]
+    rng = _rng(seed, 20, b, h)
+    omega = rng.standard_normal((rank, 3)) / np.asarray(sigma)[None, :]
+    beta = rng.uniform(0.0, 2.0 * math.pi, rank)
+    phi = math.sqrt(2.0 / rank) * np.cos(pos @ omega.T + beta[None, :])
+    w, _ = np.linalg.qr(rng.standard_normal((D, rank)))
+    p = (math.sqrt(D) * (phi @ w.T)).astype(np.float32)
+    eq = _normal(_rng(seed, 21, b, h), (S, D))
+    ek = _normal(_rng(seed, 22, b, h), (S, D))
+    inv = np.float32(1.0 / math.sqrt(2.0))
+    return (to_bf16_bits((eq + p) * inv), to_bf16_bits((ek + p) * inv),
+            to_bf16_bits(_normal(_rng(seed, 23, b, h), (S, D))))
+
+
+def gen_video(seed, B, H, D, grid=(21, 30, 52), sigma=(2.0, 4.0, 4.0), rank=64, workers=None):
+    """Video-DiT-like Q/K/V on a (frames, rows, cols) token grid; S = prod(grid).
+
+    Heads are independent random streams, generated in parallel threads."""
+    from concurrent.futures import ThreadPoolExecutor
     S = int(np.prod(grid))
     pos = video_positions(*grid)
-    q = np.empty((B, S, H, D), np.uint16)
-    k = np.empty((B, S, H, D), np.uint16)
-    v = np.empty((B, S, H, D), np.uint16)
-    for b in range(B):
-        for h in range(H):
-            rng = _rng(seed, 20, b, h)
-            omega = rng.standard_normal((rank, 3)) / np.asarray(sigma)[None, :]
-            beta = rng.uniform(0.0, 2.0 * math.pi, rank)
-            phi = math.sqrt(2.0 / rank) * np.cos(pos @ omega.T + beta[None, :])
-            w, _ = np.linalg.qr(rng.standard_normal((D, rank)))
-            p = math.sqrt(D) * (phi @ w.T)
-            eq = _normal(_rng(seed, 21, b, h), (S, D))
-            ek = _normal(_rng(seed, 22, b, h), (S, D))
-            q[b, :, h] = to_bf16_bits((eq + p) / math.sqrt(2.0))
-            k[b, :, h] = to_bf16_bits((ek + p) / math.sqrt(2.0))
-            v[b, :, h] = to_bf16_bits(_normal(_rng(seed, 23, b, h), (S, D)))
-    return q, k, v
+    out = np.empty((3, B, H, S, D), np.uint16)
+
+    def one(bh):
+        b, h = bh
+        out[0, b, h], out[1, b, h], out[2, b, h] = _video_head(seed, b, h, D, pos, sigma, rank)
+
+    workers = workers or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(one, [(b, h) for b in range(B) for h in range(H)]))
+    qkv = np.ascontiguousarray(out.transpose(0, 1, 3, 2, 4))
+    return qkv[0], qkv[1], qkv[2]
 
 
 def gen_bitmask(seed, B, Hkv, n_q_blocks, n_kv_blocks, n_set, garbage_padding=False):
