@@ -1,0 +1,305 @@
+// mainloop.h -- the pipelined key-tile loop shared by the skip-softmax, N:M and proxy kernels.
+//
+// One workgroup of NW wavefronts owns NW*64 query rows and walks a sequence of 64-key tiles
+// ("steps") given by a policy object.  K and V tiles are copied HBM/L2 -> LDS with buffer loads
+// that write LDS directly (no staging registers), double-buffered.  Scores run two tiles ahead of
+// the softmax, so every tile is decided one full iteration before its V tile is needed:
+//
+//   iteration j (S(j), S(j+1) computed and decided; in flight: V(j), K(j+2), V(j+1))
+//     1  wait for V(j) and K(j+2); barrier
+//     2  issue K(j+3)
+//     3  [kept(j)]   softmax(j) fused with O += P(j) V(j), 16 keys at a time (VALU || MFMA)
+//     4  S(j+2) = QK^T(j+2) into the registers S(j) used; mask; row max
+//     5  wave vote "some row of j+2 not negligible"; barrier; keep(j+2) = OR of the votes
+//     6  [kept(j+2)] issue V(j+2)
+//
+// A skipped tile costs its QK^T, row max and vote only: no exponentials, no V traffic, no P.V.
+// Loads are issued in the order ..., V(j), K(j+2), V(j+1), K(j+3), V(j+2), ...; each wait is an
+// explicit s_waitcnt vmcnt that leaves only the newest V in flight.  Cross-wave barriers are
+// "s_waitcnt lgkmcnt(0); s_barrier" (vote stores must land, prefetches must not drain).
+//
+// Exponent reference: P = 2^(t - m_ref), m_ref raised (and O, l rescaled) only when a kept tile's
+// row max exceeds it by more than kRescaleSlack, so P <= 2^kRescaleSlack; numerator and
+// denominator share the reference.  The skip decision uses the exact fp32 running max mt of the
+// kept tiles' row maxima, updated as soon as a tile is decided.
+#pragma once
+
+#include "tile_core.h"
+
+namespace sa {
+
+constexpr float kRescaleSlack = 8.f;
+
+template <int D, int NW>
+struct Smem {
+  char k[2][kKeysPerTile * D * 2];
+  char v[2][kKeysPerTile * D * 2];
+  int vote[2][NW];
+};
+
+// One step's K and V sources: buffer-resource bases already offset to the tile's first row, and
+// the number of valid bytes from those bases (rows past the end read as zeros).
+struct TileSrc {
+  const __bf16* k;
+  const __bf16* v;
+  int k_bytes, v_bytes;
+  int k_stride_b, v_stride_b;
+};
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N), leaving expcnt and lgkmcnt alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int D, int NW>
+struct Dma {
+  static constexpr int kTileBytes = kKeysPerTile * D * 2;
+  static constexpr int kPerWave = kTileBytes / 1024 / NW;   // 1 KiB per wave-wide instruction
+  static constexpr int kRowsPerInst = 1024 / (D * 2);
+  static constexpr int kChunksPerRow = D / 8;
+  static_assert(kPerWave >= 1 && kTileBytes % (1024 * NW) == 0, "tile must split over the waves");
+
+  // Copy a 64-row tile into the LDS tile at `lds` (swizzled layout of tile_core.h).  Lane l of
+  // instruction i lands at byte 1024*(wave*kPerWave + i) + 16*l, i.e. row r, physical chunk p; it
+  // fetches logical chunk p ^ f(r), so logical chunk c of row r ends at physical c ^ f(r).
+  static __device__ __forceinline__ void copy(char* lds, const __bf16* base, int bytes,
+                                              int stride_b, int wave, int lane) {
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int inst = wave * kPerWave + i;
+      const int row = inst * kRowsPerInst + lane / kChunksPerRow;
+      const int chunk = chunk_swizzle<D>(row, lane % kChunksPerRow);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(lds + inst * 1024), 16,
+          row * stride_b + chunk * 16, 0, 0, 0);
+    }
+  }
+};
+
+__device__ __forceinline__ void tile_row_max(const f32x16 (&s)[2][2], float c32, float (&M)[2]) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+    M[qb] = half_max(mx) * c32;
+  }
+}
+
+// Per-tile state: row maxima (log2 domain), N:M keep bits, decision.
+struct TileState {
+  float M[2];
+  uint32_t kbits[2];
+  bool keep;
+};
+
+// Softmax of a kept tile fused with its P.V product.  For each 16-key chunk: exponentials of the
+// chunk (VALU), then the 8 MFMAs that consume them, so the VALU work of one chunk overlaps the
+// MFMAs of the previous one.  keep bits (N:M) zero dropped keys; Pol::weight (proxy) scales each
+// key's row-sum term.
+template <int D, class Pol>
+__device__ __forceinline__ void softmax_pv(const Pol& pol, int step, const f32x16 (&s)[2][2],
+                                           const TileState& ts, float (&mref)[2], float (&l)[2],
+                                           f32x16 (&o)[D / 32][2], const char* ldsV, float c32,
+                                           int lane) {
+  bool need = false;
+  float cand[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    cand[qb] = fmaxf(mref[qb], ts.M[qb]);
+    need |= cand[qb] > mref[qb] + kRescaleSlack;   // also true when mref = -inf, M finite
+  }
+  if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+    agpr_read_guard<D>(o);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float alpha = mref[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref[qb] - cand[qb]);
+      l[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db][qb] *= alpha;
+      mref[qb] = cand[qb];
+    }
+    agpr_write_guard<D>(o);
+  }
+  float muse[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) muse[qb] = mref[qb] == -INFINITY ? 0.f : mref[qb];
+  bool weighted = false;
+  if constexpr (Pol::kWeighted) weighted = pol.weighted(step);
+
+  const int g = lane >> 4, j = lane & 15, h = lane >> 5;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      bf16x8 pb[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float rs = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * c + e;
+          float p = __builtin_amdgcn_exp2f(s[kb][qb][r] * c32 - muse[qb]);
+          if constexpr (Pol::kFilter) p = ((ts.kbits[qb] >> (kb * 16 + r)) & 1u) ? p : 0.f;
+          if constexpr (Pol::kWeighted) {
+            rs += weighted ? p * pol.weight(step, kb, r, lane) : p;
+          } else {
+            rs += p;
+          }
+          pb[qb][e] = (__bf16)p;
+        }
+        l[qb] += rs;
+      }
+      // V^T operand of these 16 keys for each 32-wide d block (transpose reads), then MFMAs
+      const int row = kb * 32 + c * 16 + 4 * h + (j >> 2);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int col = db * 32 + 16 * (g & 1) + 4 * (j & 3);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(ldsV + tile_offset<D>(row, col)));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(ldsV + tile_offset<D>(row + 8, col)));
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        mfma32_agpr(o[db][0], a, pb[0]);
+        mfma32_agpr(o[db][1], a, pb[1]);
+      }
+    }
+  }
+}
+
+// The step loop.  Pol provides:
+//   int steps() const;  TileSrc src(int step) const;
+//   void mask(int step, f32x16 (&s)[2][2], int lane) const;        -inf for masked keys
+//   static constexpr bool kDecide, kFilter, kWeighted;
+//   bool negligible(const float (&M)[2], const float (&mt)[2], int lane) const;   [kDecide]
+//   void filter(int step, const f32x16 (&s)[2][2], uint32_t (&bits)[2], int lane) const; [kFilter]
+//   bool weighted(int step) const; float weight(int step, int kb, int r, int lane) const; [kWeighted]
+//   void record(int step, bool keep, const float (&M)[2], int wave, int lane, int tid);
+// On return o, mref and l hold the unnormalised accumulator (AGPRs), exponent reference and
+// row-sum partials of this lane (l still to be summed over the two lane halves).
+template <int D, int NW, class Pol>
+struct Mainloop {
+  using DmaT = Dma<D, NW>;
+  static constexpr int kN = DmaT::kPerWave;   // loads per tile per lane
+
+  Pol& pol;
+  Smem<D, NW>& sm;
+  const bf16x8 (&qf)[2][D / 16];
+  f32x16 (&o)[D / 32][2];
+  float (&mref)[2];
+  float (&l)[2];
+  float c32;
+  int wave, lane, tid, n;
+  float mt[2] = {-INFINITY, -INFINITY};   // running max of kept tiles' maxima (decision state)
+
+  __device__ __forceinline__ void issue_k(int step) {
+    const TileSrc t = pol.src(step);
+    DmaT::copy(sm.k[step & 1], t.k, t.k_bytes, t.k_stride_b, wave, lane);
+  }
+  __device__ __forceinline__ void issue_v(int step) {
+    const TileSrc t = pol.src(step);
+    DmaT::copy(sm.v[step & 1], t.v, t.v_bytes, t.v_stride_b, wave, lane);
+  }
+
+  // S(step) from the K tile in LDS, masked, with its row maxima and N:M bits.
+  __device__ __forceinline__ void scores(int step, f32x16 (&s)[2][2], TileState& ts) {
+    qk_tile<D>(sm.k[step & 1], qf, s, lane);
+    pol.mask(step, s, lane);
+    tile_row_max(s, c32, ts.M);
+    ts.kbits[0] = ts.kbits[1] = ~0u;
+    if constexpr (Pol::kFilter) pol.filter(step, s, ts.kbits, lane);
+  }
+
+  // Vote through LDS; one barrier.  A kept tile raises the decision max mt at once.
+  __device__ __forceinline__ void decide(int step, TileState& ts) {
+    if constexpr (Pol::kDecide) {
+      const bool wave_keep = __builtin_amdgcn_ballot_w64(!pol.negligible(ts.M, mt, lane)) != 0ull;
+      if (lane == 0) sm.vote[step & 1][wave] = wave_keep ? 1 : 0;
+    }
+    lds_barrier();
+    ts.keep = true;
+    if constexpr (Pol::kDecide) {
+      int any = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) any |= sm.vote[step & 1][w];
+      ts.keep = any != 0;
+    }
+    if (ts.keep) {
+      mt[0] = fmaxf(mt[0], ts.M[0]);
+      mt[1] = fmaxf(mt[1], ts.M[1]);
+    }
+    pol.record(step, ts.keep, ts.M, wave, lane, tid);
+  }
+
+  // iteration j: S(j) in sa (state ta), S(j+1) decided (state tb); S(j+2) is written into sa.
+  __device__ __forceinline__ void iteration(int j, f32x16 (&sa)[2][2], TileState& ta,
+                                            const TileState& tb) {
+    // 1: V(j) and K(j+2) landed; V(j+1), the newest load, may still be in flight
+    if (tb.keep) wait_vmcnt<kN>(); else wait_vmcnt<0>();
+    lds_barrier();
+    // 2: prefetch K(j+3) into the buffer K(j+1) used
+    if (j + 3 < n) issue_k(j + 3);
+    // 3: softmax(j) fused with O += P(j) V(j)
+    if (ta.keep) softmax_pv<D>(pol, j, sa, ta, mref, l, o, sm.v[j & 1], c32, lane);
+    // 4-6: S(j+2), its vote, its V tile
+    if (j + 2 < n) {
+      scores(j + 2, sa, ta);
+      decide(j + 2, ta);
+      if (ta.keep) issue_v(j + 2);
+    } else {
+      ta.keep = false;
+    }
+  }
+
+  __device__ __forceinline__ void run() {
+    if (n <= 0) return;
+    f32x16 sa[2][2], sb[2][2];
+    TileState ta, tb;
+    // prologue: K(0), K(1); S(0), keep(0), V(0); K(2); S(1), keep(1), V(1)
+    issue_k(0);
+    if (n > 1) issue_k(1);
+    if (n > 1) wait_vmcnt<kN>(); else wait_vmcnt<0>();
+    lds_barrier();
+    scores(0, sa, ta);
+    decide(0, ta);
+    if (ta.keep) issue_v(0);
+    tb.keep = false;
+    if (n > 1) {
+      if (n > 2) issue_k(2);   // K(0)'s buffer: every wave passed the vote barrier after QK(0)
+      // K(1) landed: in flight after it are V(0) (if kept) and K(2) (if any)
+      if (ta.keep && n > 2) wait_vmcnt<2 * kN>();
+      else if (ta.keep || n > 2) wait_vmcnt<kN>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      scores(1, sb, tb);
+      decide(1, tb);
+      if (tb.keep) issue_v(1);
+    }
+    for (int j = 0; j < n; j += 2) {
+      iteration(j, sa, ta, tb);
+      if (j + 1 < n) iteration(j + 1, sb, tb, ta);
+    }
+  }
+};
+
+template <int D, int NW, class Pol>
+__device__ __forceinline__ void run_mainloop(Pol& pol, Smem<D, NW>& sm,
+                                             const bf16x8 (&qf)[2][D / 16],
+                                             f32x16 (&o)[D / 32][2], float (&mref)[2],
+                                             float (&l)[2], float c32, int wave, int lane,
+                                             int tid) {
+  Mainloop<D, NW, Pol> ml{pol, sm, qf, o, mref, l, c32, wave, lane, tid, pol.steps()};
+  ml.run();
+}
+
+}  // namespace sa

@@ -7,49 +7,186 @@
 // groups aligned to key 0, ranking by the raw score q.k among all members of the group (masked
 // keys rank last), ties to the lower key index, "recent" = 0 <= row - key < R.
 //
-// Same tile skeleton as the skip-softmax kernel, every visited tile kept.  In the S^T register
+// Same pipelined loop as the skip-softmax kernel (mainloop.h), every visited tile kept.  In the S^T register
 // layout a lane holds, for one query, keys 8g + 4h + {0..3} in elements 4g..4g+3 (h = lane/32), so
 // an M = 4 group is four consecutive elements of one lane and an M = 8 group is those four plus the
 // same four elements of lane ^ 32 (one v_permlane32_swap).  Dropped keys get weight 0 in P.  The
 // running max needs no change: the group maximum always survives (rank 0 < N), so the max over
 // kept keys equals the max over allowed keys.
 #include "kernels.h"
-#include "tile_core.h"
+#include "mainloop.h"
 
 namespace sa {
 namespace {
 
-// Number of elements of the group that beat element i (higher score, or equal score and lower key
-// index).  own[0..3] are this lane's four keys in ascending key order; for M = 8, oth[0..3] are the
-// lane ^ 32 half of the group, whose keys all come before ours when own_first is false.
+// 1 when d < 0, else 0, for d the fp32 difference of two finite scores normalised by "+ 0.0f"
+// (so that equal scores give +0): the sign bit, read without a compare (a compare per pair would
+// park a lane mask in SGPRs).
+__device__ __forceinline__ int neg01(float d) { return (int)(__float_as_uint(d + 0.0f) >> 31); }
+
+// rank[i] = number of group members that beat own[i]: a higher score, or an equal score at a lower
+// key index.  own[0..3] are this lane's four keys in ascending key order; for M = 8, oth[0..3] are
+// the lane ^ 32 half of the group, whose keys all come after ours when own_first is true.  Scores
+// are finite here (masked keys enter as -FLT_MAX, which still ties only with other masked keys).
 template <int M>
 __device__ __forceinline__ void group_ranks(const float (&own)[4], const float (&oth)[4],
                                             bool own_first, int (&rank)[4]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int rk = 0;
+  for (int i = 0; i < 4; ++i) rank[i] = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j == i) continue;
-      rk += (j < i) ? (own[j] >= own[i]) : (own[j] > own[i]);
-    }
-    if constexpr (M == 8) {
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) rk += own_first ? (oth[j] > own[i]) : (oth[j] >= own[i]);
+    for (int j = i + 1; j < 4; ++j) {
+      // j comes after i: j beats i iff own[j] > own[i], otherwise i beats j
+      const int jgt = neg01(own[i] - own[j]);
+      rank[i] += jgt;
+      rank[j] += 1 - jgt;
     }
-    rank[i] = rk;
+  if constexpr (M == 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // other half after ours: it beats own[i] iff strictly greater; before ours: iff >=
+        const int gt = neg01(own[i] - oth[j]);   // oth[j] > own[i]
+        const int lt = neg01(oth[j] - own[i]);   // oth[j] < own[i]
+        rank[i] += own_first ? gt : 1 - lt;
+      }
   }
 }
+
+template <int D, int NW, int M>
+struct NmPolicy {
+  static constexpr bool kDecide = false, kFilter = true, kWeighted = false;
+  const __bf16* kslab;
+  const __bf16* vslab;
+  int k_stride_b, v_stride_b, k_bytes, v_bytes;
+  int Sq, Sk, causal, wrow0, nvis, h, r32, n, sink, recent, W;
+  uint32_t* keep_bits;
+  float* scores;
+  int64_t row_base;   // (b*Hq + hq)*Sq
+
+  __device__ __forceinline__ int steps() const { return nvis; }
+
+  __device__ __forceinline__ TileSrc src(int j) const {
+    const int k0 = j * kKeysPerTile;
+    return TileSrc{kslab + (int64_t)k0 * (k_stride_b / 2), vslab + (int64_t)k0 * (v_stride_b / 2),
+                   max(0, k_bytes - k0 * k_stride_b), max(0, v_bytes - k0 * v_stride_b),
+                   k_stride_b, v_stride_b};
+  }
+
+  __device__ __forceinline__ void mask(int j, f32x16 (&s)[2][2], int lane) const {
+    const int k0 = j * kKeysPerTile;
+    if (!((k0 + kKeysPerTile > Sk) || (causal && k0 + kKeysPerTile - 1 > wrow0))) return;
+    const int klim = Sk - k0 - 4 * h;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      int lim = klim;
+      if (causal) lim = min(lim, wrow0 + qb * 32 + r32 - k0 - 4 * h + 1);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) mask_block(s[kb][qb], kb, lim);
+    }
+  }
+
+  // keep bit (kb*16 + r) of bits[qb]: key not masked and (dense, or top-n of its group).  All
+  // per-element tests are sign-bit arithmetic; the sink/recent windows and masked keys only occur
+  // on a few tiles per row, tested once per tile.
+  __device__ __forceinline__ void filter(int j, const f32x16 (&s)[2][2], uint32_t (&bits)[2],
+                                         int lane) const {
+    const int k0 = j * kKeysPerTile;
+    const bool any_masked = (k0 + kKeysPerTile > Sk) || (causal && k0 + kKeysPerTile - 1 > wrow0);
+    const bool any_dense = k0 < sink ||
+        (recent > 0 && k0 <= wrow0 + kRowsPerWave - 1 && k0 + kKeysPerTile - 1 > wrow0 - recent);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int row = wrow0 + qb * 32 + r32;
+      uint32_t kb_bits = 0u;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          float own[4], oth[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            own[e] = fmaxf(s[kb][qb][4 * gi + e], -3.402823466e38f);   // masked: finite sentinel
+            oth[e] = own[e];
+            if constexpr (M == 8) oth[e] = other_half(own[e], lane);
+          }
+          int rank[4];
+          group_ranks<M>(own, oth, h == 0, rank);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)   // top-n: rank - n < 0
+            kb_bits |= ((uint32_t)(rank[e] - n) >> 31) << (kb * 16 + 4 * gi + e);
+        }
+      }
+      if (any_dense) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + (r >> 2) * 8 + 4 * h + (r & 3);
+            const int d = row - key;   // dense: key < sink, or 0 <= d < recent
+            const uint32_t dense = ((uint32_t)(key - sink) >> 31) |
+                                   ((~(uint32_t)d >> 31) & ((uint32_t)(d - recent) >> 31));
+            kb_bits |= dense << (kb * 16 + r);
+          }
+      }
+      if (any_masked) {   // masked keys hold -inf
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t x = __float_as_uint(s[kb][qb][r]) ^ 0xFF800000u;   // 0 iff -inf
+            const uint32_t live = (x | (0u - x)) >> 31;
+            kb_bits &= ~((live ^ 1u) << (kb * 16 + r));
+          }
+      }
+      bits[qb] = kb_bits;
+      if (keep_bits != nullptr || scores != nullptr) export_row(k0, row, qb, kb_bits, s, lane);
+    }
+  }
+
+  // debug exports of one query row: keep-bit words and raw scores
+  __device__ __forceinline__ void export_row(int k0, int row, int qb, uint32_t kb_bits,
+                                             const f32x16 (&s)[2][2], int lane) const {
+    // lanes l and l^32 hold the same row: both stay active through the swap
+    const int64_t rbase = row_base + row;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      uint32_t word = 0u;   // this lane's 16 bits of the 32-key word, merged with lane^32's
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        word |= ((kb_bits >> (kb * 16 + r)) & 1u) << ((r >> 2) * 8 + 4 * h + (r & 3));
+      word |= __float_as_uint(other_half(__uint_as_float(word), lane));
+      if (row < Sq) {
+        if (keep_bits != nullptr && h == 0 && k0 + kb * 32 < Sk)
+          keep_bits[rbase * W + k0 / 32 + kb] = word;
+        if (scores != nullptr) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + tile_key(kb, r, lane);
+            if (key < Sk) scores[rbase * Sk + key] = s[kb][qb][r];
+          }
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ bool negligible(const float (&)[2], const float (&)[2], int) const {
+    return false;
+  }
+  __device__ __forceinline__ void record(int, bool, const float (&)[2], int, int, int) {}
+};
 
 template <int D, int NW, int M>
 __global__ __launch_bounds__(NW * 64) void nm_softmax_kernel(NmArgs a) {
   constexpr int BR = NW * kRowsPerWave;
   constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) char ldsK[kKeysPerTile * D * 2];
-  __shared__ __attribute__((aligned(16))) char ldsV[kKeysPerTile * D * 2];
+  __shared__ __attribute__((aligned(1024))) Smem<D, NW> sm;
 
   const AttnGeom& g = a.g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r32 = lane & 31;
   const int nQT = (g.Sq + BR - 1) / BR;
   const int nKT = (g.Sk + kKeysPerTile - 1) / kKeysPerTile;
@@ -68,156 +205,51 @@ __global__ __launch_bounds__(NW * 64) void nm_softmax_kernel(NmArgs a) {
 
   const int row0 = qt * BR;
   const int wrow0 = row0 + wave * kRowsPerWave;
-  const int wrows = g.Sq - wrow0;
   const int last_row = min(row0 + BR, g.Sq) - 1;
   const int nvis = g.causal ? min(nKT, last_row / kKeysPerTile + 1) : nKT;
   const int W = (g.Sk + 31) / 32;
 
   const auto qsrc = slab_rsrc((const __bf16*)g.q + b * g.qs[0] + hq * g.qs[2], g.qs[1], g.Sq, D);
-  const auto ksrc = slab_rsrc((const __bf16*)g.k + b * g.ks[0] + hk * g.ks[2], g.ks[1], g.Sk, D);
-  const auto vsrc = slab_rsrc((const __bf16*)g.v + b * g.vs[0] + hk * g.vs[2], g.vs[1], g.Sk, D);
-
   bf16x8 qf[2][D / 16];
   load_q_frags<D>(qf, qsrc, g.qs[1], wrow0, lane);
+  park_q_in_agprs<D>(qf);
+
+  NmPolicy<D, NW, M> pol;
+  pol.kslab = (const __bf16*)g.k + b * g.ks[0] + hk * g.ks[2];
+  pol.vslab = (const __bf16*)g.v + b * g.vs[0] + hk * g.vs[2];
+  pol.k_stride_b = (int)(g.ks[1] * 2);
+  pol.v_stride_b = (int)(g.vs[1] * 2);
+  pol.k_bytes = (int)(((int64_t)(g.Sk - 1) * g.ks[1] + D) * 2);
+  pol.v_bytes = (int)(((int64_t)(g.Sk - 1) * g.vs[1] + D) * 2);
+  pol.Sq = g.Sq;
+  pol.Sk = g.Sk;
+  pol.causal = g.causal;
+  pol.wrow0 = wrow0;
+  pol.nvis = nvis;
+  pol.h = h;
+  pol.r32 = r32;
+  pol.n = a.n;
+  pol.sink = a.sink;
+  pol.recent = a.recent;
+  pol.W = W;
+  pol.keep_bits = a.keep_bits;
+  pol.scores = a.scores;
+  pol.row_base = ((int64_t)b * g.Hq + hq) * g.Sq;
 
   f32x16 o[D / 32][2];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db][0] = o[db][1] = f32x16{};
-  float m[2] = {-INFINITY, -INFINITY};
+  float mref[2] = {-INFINITY, -INFINITY};
   float l[2] = {0.f, 0.f};
+  run_mainloop<D, NW>(pol, sm, qf, o, mref, l, g.c32, wave, lane, tid);
 
-  for (int j = 0; j < nvis; ++j) {
-    const int k0 = j * kKeysPerTile;
-    stage_tile<D, NT>(ldsK, ksrc, g.ks[1], k0, tid);
-    stage_tile<D, NT>(ldsV, vsrc, g.vs[1], k0, tid);
-    __syncthreads();
-
-    f32x16 s[2][2];
-    qk_tile<D>(ldsK, qf, s, lane);
-
-    // causal / out-of-range keys -> -inf (same limit form as the skip kernel)
-    const bool need_mask = (k0 + kKeysPerTile > g.Sk) ||
-                           (g.causal && k0 + kKeysPerTile - 1 > wrow0);
-    if (need_mask) {
-      const int klim = g.Sk - k0 - 4 * h;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        int lim = klim;
-        if (g.causal) lim = min(lim, wrow0 + qb * 32 + r32 - k0 - 4 * h + 1);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kb * 32 + (r >> 2) * 8 + (r & 3) >= lim) s[kb][qb][r] = -INFINITY;
-      }
-    }
-
-    // keep mask: bit (kb*16 + r) of keep[qb]
-    uint32_t keep[2] = {0u, 0u};
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int row = wrow0 + qb * 32 + r32;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          float own[4], oth[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            own[e] = s[kb][qb][4 * gi + e];
-            oth[e] = own[e];
-            if constexpr (M == 8) oth[e] = other_half(own[e], lane);
-          }
-          int rank[4];
-          group_ranks<M>(own, oth, h == 0, rank);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int key = k0 + kb * 32 + gi * 8 + 4 * h + e;
-            const bool dense = key < a.sink || (row - key >= 0 && row - key < a.recent);
-            const bool masked = key >= g.Sk || (g.causal && key > row);
-            if (!masked && (dense || rank[e] < a.n)) keep[qb] |= 1u << (kb * 16 + 4 * gi + e);
-          }
-        }
-      }
-    }
-
-    if (a.keep_bits != nullptr || a.scores != nullptr) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int row = wrow0 + qb * 32 + r32;
-        if (row >= g.Sq) continue;
-        const int64_t rbase = ((int64_t)b * g.Hq + hq) * g.Sq + row;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          // this lane's 16 bits of the 32-key word k0/32 + kb, merged with the other half's
-          uint32_t word = 0u;
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if ((keep[qb] >> (kb * 16 + r)) & 1u) word |= 1u << ((r >> 2) * 8 + 4 * h + (r & 3));
-          word |= __float_as_uint(other_half(__uint_as_float(word), lane));
-          if (a.keep_bits != nullptr && h == 0 && k0 + kb * 32 < g.Sk)
-            a.keep_bits[rbase * W + k0 / 32 + kb] = word;
-          if (a.scores != nullptr) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = k0 + tile_key(kb, r, lane);
-              if (key < g.Sk) a.scores[rbase * g.Sk + key] = s[kb][qb][r];
-            }
-          }
-        }
-      }
-    }
-
-    // online softmax; dropped keys contribute exactly 0
-    float M_[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      M_[qb] = half_max(mx) * g.c32;
-    }
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float m_new = fmaxf(m[qb], M_[qb]);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_use);
-      l[qb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) o[db][qb] *= alpha;
-      m[qb] = m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(s[kb][qb][r] * g.c32 - m_use);
-          const float p = ((keep[qb] >> (kb * 16 + r)) & 1u) ? e : 0.f;
-          s[kb][qb][r] = p;
-          rs += p;
-        }
-      l[qb] += rs;
-    }
-    bf16x8 pb[2][2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) pb[kb][c][qb] = p_operand(s[kb][qb], c);
-    pv_tile<D>(ldsV, pb, o, lane);
-    __syncthreads();   // all waves done with this K/V tile before it is overwritten
-  }
-
-  // keep-bit words of tiles never visited (causal): all zero
+  // keep-bit words and scores of tiles never visited (causal): zero / -inf
   if (a.keep_bits != nullptr) {
     const int wfirst = nvis * (kKeysPerTile / 32);
     for (int rr = tid; rr < BR; rr += NT) {
       const int row = row0 + rr;
       if (row >= g.Sq) continue;
-      const int64_t rbase = ((int64_t)b * g.Hq + hq) * g.Sq + row;
+      const int64_t rbase = pol.row_base + row;
       for (int w = wfirst; w < W; ++w) a.keep_bits[rbase * W + w] = 0u;
     }
   }
@@ -226,11 +258,12 @@ __global__ __launch_bounds__(NW * 64) void nm_softmax_kernel(NmArgs a) {
     for (int rr = 0; rr < BR; ++rr) {
       const int row = row0 + rr;
       if (row >= g.Sq) break;
-      const int64_t rbase = ((int64_t)b * g.Hq + hq) * g.Sq + row;
+      const int64_t rbase = pol.row_base + row;
       for (int key = kfirst + tid; key < g.Sk; key += NT) a.scores[rbase * g.Sk + key] = -INFINITY;
     }
   }
 
+  agpr_read_guard<D>(o);
   float inv[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -238,11 +271,11 @@ __global__ __launch_bounds__(NW * 64) void nm_softmax_kernel(NmArgs a) {
     inv[qb] = lt > 0.f ? 1.f / lt : 0.f;
     const int row = wrow0 + qb * 32 + r32;
     if (a.lse != nullptr && h == 0 && row < g.Sq)
-      a.lse[((int64_t)b * g.Hq + hq) * g.Sq + row] =
-          lt > 0.f ? (m[qb] + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
+      a.lse[pol.row_base + row] =
+          lt > 0.f ? (mref[qb] + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
   }
   __bf16* op = (__bf16*)g.o + b * g.os[0] + (int64_t)wrow0 * g.os[1] + hq * g.os[2];
-  store_o<D>(op, g.os[1], wrows, o, inv, lane);
+  store_o<D>(op, g.os[1], g.Sq - wrow0, o, inv, lane);
 }
 
 template <int D, int NW, int M>

@@ -8,26 +8,107 @@
 //     O = [sum_t e^{s_t} v_t + sum_j e^{s^_j} Vsum_j] / [sum_t e^{s_t} + sum_j c_j e^{s^_j}],
 //     s = scale * q.k,  c_j = min(Bk, Sk - j*Bk).
 //
-// One workgroup = one (batch, query head, query block).  The exact part walks the route stream
-// (n_exact, exact_idx) of the query block's (batch, KV head) row: each exact block is one or two
-// 64-key tiles of raw K/V.  The proxy part, when enabled, treats the summary rows as keys: tiles of
-// 64 summaries (K = k_mean rows, V = v_sum rows), rows whose proxy_keep bit is clear masked to
-// -inf, and the row sum weighted by c_j.  Both parts share the online softmax state.
+// One workgroup = one (batch, query head, query block), on the pipelined loop of mainloop.h.  The
+// steps are first the exact blocks of the route stream (n_exact, exact_idx) of the query block's
+// (batch, KV head) row, each one or two 64-key tiles of raw K/V, then, when enabled, the proxy
+// tiles: 64 summary rows at a time (K = k_mean rows, V = v_sum rows), rows whose proxy_keep bit is
+// clear masked to -inf, and the row sum weighted by c_j.  Both parts share the online softmax.
 #include "kernels.h"
-#include "tile_core.h"
+#include "mainloop.h"
 
 namespace sa {
 namespace {
 
+// Exact steps (pipelined main loop): the 64-key tiles of the exact blocks, in ascending order.
+template <int D, int NW>
+struct ExactPolicy {
+  static constexpr bool kDecide = false, kFilter = false, kWeighted = false;
+  const __bf16* kslab;
+  const __bf16* vslab;
+  const int32_t* exact;  // ascending exact block indices of this query block
+  int k_stride_b, v_stride_b, k_bytes, v_bytes;
+  int Sk, Bk, sub, n_exact, h;
+
+  __device__ __forceinline__ int steps() const { return n_exact * sub; }
+
+  __device__ __forceinline__ int first_key(int step) const {
+    const int blk = __builtin_amdgcn_readfirstlane(exact[step / sub]);
+    return blk * Bk + (step % sub) * kKeysPerTile;
+  }
+
+  __device__ __forceinline__ TileSrc src(int step) const {
+    const int k0 = first_key(step);
+    return TileSrc{kslab + (int64_t)k0 * (k_stride_b / 2), vslab + (int64_t)k0 * (v_stride_b / 2),
+                   max(0, k_bytes - k0 * k_stride_b), max(0, v_bytes - k0 * v_stride_b),
+                   k_stride_b, v_stride_b};
+  }
+
+  // keys past Sk exist only in the final partial block
+  __device__ __forceinline__ void mask(int step, f32x16 (&s)[2][2], int lane) const {
+    const int k0 = first_key(step);
+    if (k0 + kKeysPerTile <= Sk) return;
+    const int lim = Sk - k0 - 4 * h;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      mask_block(s[kb][0], kb, lim);
+      mask_block(s[kb][1], kb, lim);
+    }
+  }
+
+  __device__ __forceinline__ bool negligible(const float (&)[2], const float (&)[2], int) const {
+    return false;
+  }
+  __device__ __forceinline__ void filter(int, const f32x16 (&)[2][2], uint32_t (&)[2], int) const {}
+  __device__ __forceinline__ void record(int, bool, const float (&)[2], int, int, int) {}
+};
+
+// Proxy tiles: 64 summary rows at a time; rows whose proxy_keep bit is clear (or past nKB) are
+// masked, and each kept row's row-sum term is weighted by its token mass c_j.
+struct SummaryPolicy {
+  static constexpr bool kFilter = false, kWeighted = true;
+  const uint32_t* keep;  // proxy_keep words of this query block
+  int Bk, nKB, Wd, last_len, h;
+
+  __device__ __forceinline__ bool weighted(int) const { return true; }
+
+  __device__ __forceinline__ void mask(int t, f32x16 (&s)[2][2]) const {
+    const int r0 = t * kKeysPerTile;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int wd = (r0 >> 5) + kb;
+      uint32_t bits = 0u;
+      if (wd < Wd) {
+        const int nbits = nKB - 32 * wd;   // >= 1; clears stray padding bits
+        bits = keep[wd] & (nbits >= 32 ? 0xFFFFFFFFu : ((1u << nbits) - 1u));
+      }
+      const uint32_t lane_bits = bits >> (4 * h);   // element r holds bit (r/4)*8 + r%4 of these
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = (int)((lane_bits >> ((r >> 2) * 8 + (r & 3))) & 1u) - 1;   // -1: drop
+        float o0, o1;
+        asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(o0) : "v"(m), "v"(-INFINITY), "v"(s[kb][0][r]));
+        asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(o1) : "v"(m), "v"(-INFINITY), "v"(s[kb][1][r]));
+        s[kb][0][r] = o0;
+        s[kb][1][r] = o1;
+      }
+    }
+  }
+
+  // token mass of summary row j: the full block, or the final block's true length
+  __device__ __forceinline__ float weight(int t, int kb, int r, int lane) const {
+    const int j = t * kKeysPerTile + tile_key(kb, r, lane);
+    return (float)(j == nKB - 1 ? last_len : Bk);
+  }
+};
+
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void proxy_kernel(ProxyArgs a) {
   constexpr int BR = NW * kRowsPerWave;
-  constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) char ldsK[kKeysPerTile * D * 2];
-  __shared__ __attribute__((aligned(16))) char ldsV[kKeysPerTile * D * 2];
+  __shared__ __attribute__((aligned(1024))) Smem<D, NW> sm;
 
   const AttnGeom& g = a.g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r32 = lane & 31;
   const int Bk = g.block_k;
   const int nQB = (g.Sq + BR - 1) / BR;
@@ -47,130 +128,68 @@ __global__ __launch_bounds__(NW * 64) void proxy_kernel(ProxyArgs a) {
 
   const int row0 = qb_blk * BR;
   const int wrow0 = row0 + wave * kRowsPerWave;
-  const int wrows = g.Sq - wrow0;
   const int64_t route_row = ((int64_t)b * g.Hkv + hk) * nQB + qb_blk;
-  const int n_exact = min(max(a.n_exact[route_row], 0), nKB);   // never index past the row
-  const int32_t* exact = a.exact_idx + route_row * nKB;
-  const uint32_t* keep_bits = a.proxy_keep + route_row * Wd;
 
   const auto qsrc = slab_rsrc((const __bf16*)g.q + b * g.qs[0] + hq * g.qs[2], g.qs[1], g.Sq, D);
-  const auto ksrc = slab_rsrc((const __bf16*)g.k + b * g.ks[0] + hk * g.ks[2], g.ks[1], g.Sk, D);
-  const auto vsrc = slab_rsrc((const __bf16*)g.v + b * g.vs[0] + hk * g.vs[2], g.vs[1], g.Sk, D);
-
   bf16x8 qf[2][D / 16];
   load_q_frags<D>(qf, qsrc, g.qs[1], wrow0, lane);
+  park_q_in_agprs<D>(qf);
+
+  ExactPolicy<D, NW> pol;
+  pol.kslab = (const __bf16*)g.k + b * g.ks[0] + hk * g.ks[2];
+  pol.vslab = (const __bf16*)g.v + b * g.vs[0] + hk * g.vs[2];
+  pol.exact = a.exact_idx + route_row * nKB;
+  pol.k_stride_b = (int)(g.ks[1] * 2);
+  pol.v_stride_b = (int)(g.vs[1] * 2);
+  pol.k_bytes = (int)(((int64_t)(g.Sk - 1) * g.ks[1] + D) * 2);
+  pol.v_bytes = (int)(((int64_t)(g.Sk - 1) * g.vs[1] + D) * 2);
+  pol.Sk = g.Sk;
+  pol.Bk = Bk;
+  pol.sub = Bk / kKeysPerTile;
+  // never index past the route row, whatever the caller passed
+  pol.n_exact = min(max(__builtin_amdgcn_readfirstlane(a.n_exact[route_row]), 0), nKB);
+  pol.h = h;
 
   f32x16 o[D / 32][2];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db][0] = o[db][1] = f32x16{};
-  float m[2] = {-INFINITY, -INFINITY};
+  float mref[2] = {-INFINITY, -INFINITY};
   float l[2] = {0.f, 0.f};
+  run_mainloop<D, NW>(pol, sm, qf, o, mref, l, g.c32, wave, lane, tid);
 
-  const int sub = Bk / kKeysPerTile;                       // 64-key tiles per semantic block
-  const int n_proxy_tiles = a.use_proxy ? (nKB + kKeysPerTile - 1) / kKeysPerTile : 0;
-  const int n_steps = n_exact * sub + n_proxy_tiles;
-  const int last_len = g.Sk - (nKB - 1) * Bk;              // tokens in the final (partial) block
-
-  for (int step = 0; step < n_steps; ++step) {
-    const bool proxy = step >= n_exact * sub;
-    int k0;
-    if (!proxy) {
-      k0 = exact[step / sub] * Bk + (step % sub) * kKeysPerTile;
-      stage_tile<D, NT>(ldsK, ksrc, g.ks[1], k0, tid);
-      stage_tile<D, NT>(ldsV, vsrc, g.vs[1], k0, tid);
-    } else {
-      k0 = (step - n_exact * sub) * kKeysPerTile;           // first summary row of the tile
-      const int64_t sbase = ((int64_t)b * g.Hkv + hk) * nKB * D;
-      const auto kmsrc = slab_rsrc((const __bf16*)a.k_mean + sbase, D, nKB, D);
-      const auto vssrc = slab_rsrc((const __bf16*)a.v_sum + sbase, D, nKB, D);
-      stage_tile<D, NT>(ldsK, kmsrc, D, k0, tid);
-      stage_tile<D, NT>(ldsV, vssrc, D, k0, tid);
+  // proxy tiles: summaries as keys, one tile at a time
+  if (a.use_proxy) {
+    SummaryPolicy sp;
+    sp.keep = a.proxy_keep + route_row * Wd;
+    sp.Bk = Bk;
+    sp.nKB = nKB;
+    sp.Wd = Wd;
+    sp.last_len = g.Sk - (nKB - 1) * Bk;
+    sp.h = h;
+    const int64_t sbase = ((int64_t)b * g.Hkv + hk) * nKB * D;
+    const __bf16* kmean = (const __bf16*)a.k_mean + sbase;
+    const __bf16* vsum = (const __bf16*)a.v_sum + sbase;
+    const int n_tiles = (nKB + kKeysPerTile - 1) / kKeysPerTile;
+    for (int t = 0; t < n_tiles; ++t) {
+      const int r0 = t * kKeysPerTile;
+      const int bytes = (nKB - r0) * D * 2;
+      lds_barrier();   // every wave is done with the buffers the loop above (or tile t-1) used
+      Dma<D, NW>::copy(sm.k[0], kmean + (int64_t)r0 * D, bytes, D * 2, wave, lane);
+      Dma<D, NW>::copy(sm.v[0], vsum + (int64_t)r0 * D, bytes, D * 2, wave, lane);
+      wait_vmcnt<0>();
+      lds_barrier();
+      f32x16 s[2][2];
+      qk_tile<D>(sm.k[0], qf, s, lane);
+      sp.mask(t, s);
+      TileState ts;
+      tile_row_max(s, g.c32, ts.M);
+      ts.kbits[0] = ts.kbits[1] = ~0u;
+      ts.keep = true;
+      softmax_pv<D>(sp, t, s, ts, mref, l, o, sm.v[0], g.c32, lane);
     }
-    __syncthreads();
-
-    f32x16 s[2][2];
-    qk_tile<D>(ldsK, qf, s, lane);
-
-    if (!proxy) {
-      // keys past Sk (final partial block) -> -inf
-      if (k0 + kKeysPerTile > g.Sk) {
-        const int lim = g.Sk - k0 - 4 * h;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (kb * 32 + (r >> 2) * 8 + (r & 3) >= lim) s[kb][qb][r] = -INFINITY;
-      }
-    } else {
-      // summaries not selected by proxy_keep (or past nKB) -> -inf
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int wd = (k0 >> 5) + kb;
-        uint32_t bits = 0u;
-        if (wd < Wd) {
-          const int nbits = nKB - 32 * wd;   // >= 1; clears stray padding bits
-          bits = keep_bits[wd] & (nbits >= 32 ? 0xFFFFFFFFu : ((1u << nbits) - 1u));
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int bit = (r >> 2) * 8 + 4 * h + (r & 3);
-          if (!((bits >> bit) & 1u)) {
-            s[kb][0][r] = -INFINITY;
-            s[kb][1][r] = -INFINITY;
-          }
-        }
-      }
-    }
-
-    float M_[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      M_[qb] = half_max(mx) * g.c32;
-    }
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float m_new = fmaxf(m[qb], M_[qb]);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_use);
-      l[qb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) o[db][qb] *= alpha;
-      m[qb] = m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(s[kb][qb][r] * g.c32 - m_use);
-          s[kb][qb][r] = p;
-          if (!proxy) {
-            rs += p;
-          } else {
-            // token mass of summary row j: the full block, or the final block's true length
-            const int j = k0 + tile_key(kb, r, lane);
-            rs += p * (float)(j == nKB - 1 ? last_len : Bk);
-          }
-        }
-      l[qb] += rs;
-    }
-    bf16x8 pb[2][2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) pb[kb][c][qb] = p_operand(s[kb][qb], c);
-    pv_tile<D>(ldsV, pb, o, lane);
-    __syncthreads();
   }
 
+  agpr_read_guard<D>(o);
   float inv[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -179,10 +198,10 @@ __global__ __launch_bounds__(NW * 64) void proxy_kernel(ProxyArgs a) {
     const int row = wrow0 + qb * 32 + r32;
     if (a.lse != nullptr && h == 0 && row < g.Sq)
       a.lse[((int64_t)b * g.Hq + hq) * g.Sq + row] =
-          lt > 0.f ? (m[qb] + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
+          lt > 0.f ? (mref[qb] + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
   }
   __bf16* op = (__bf16*)g.o + b * g.os[0] + (int64_t)wrow0 * g.os[1] + hq * g.os[2];
-  store_o<D>(op, g.os[1], wrows, o, inv, lane);
+  store_o<D>(op, g.os[1], g.Sq - wrow0, o, inv, lane);
 }
 
 template <int D, int NW>

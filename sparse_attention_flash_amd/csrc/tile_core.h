@@ -110,6 +110,35 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Register classes of the two contractions are fixed by hand (inline asm): the Q^T operand and the
+// O accumulator live in AGPRs, the score accumulators in VGPRs where the softmax arithmetic reads
+// them.  The compiler's hazard recognizer does not see inside inline asm, so the wait states it
+// would insert are written out: qk_result_guard() between the last QK MFMA and the first VALU read
+// of the scores, a leading s_nop before MFMAs whose operands VALU code just wrote.
+
+// Move the Q^T fragments into AGPRs (they are only ever MFMA operands).
+template <int D>
+__device__ __forceinline__ void park_q_in_agprs(bf16x8 (&qf)[2][D / 16]) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+a"(qf[qb][ks]));
+}
+
+__device__ __forceinline__ void mfma32_qk_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma32_qk(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+// Wait states between the QK MFMAs writing the scores and VALU code reading them (a 32x32x16 MFMA
+// has 8 passes; 20 wait states cover it with margin).  Tied to the score registers so that it sits
+// exactly between the last MFMA and the first read.
+__device__ __forceinline__ void qk_result_guard(f32x16 (&s)[2][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+               : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1]));
+}
+
 // S^T for one 64-key tile: s[kb][qb] is the 32x32 block keys 32*kb.., queries 32*qb..
 // Element r of lane l: key 32*kb + (r/4)*8 + 4*(l/32) + r%4, query 32*qb + l%32.
 template <int D>
@@ -118,16 +147,34 @@ __device__ __forceinline__ void qk_tile(const char* ldsK, const bf16x8 (&qf)[2][
   const int h = lane >> 5, r32 = lane & 31;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    s[kb][0] = f32x16{};
-    s[kb][1] = f32x16{};
     const int row = kb * 32 + r32;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(
           ldsK + row * (D * 2) + chunk_swizzle<D>(row, 2 * ks + h) * 16);
-      s[kb][0] = mfma32(a, qf[0][ks], s[kb][0]);
-      s[kb][1] = mfma32(a, qf[1][ks], s[kb][1]);
+      if (ks == 0) {
+        mfma32_qk_first(s[kb][0], a, qf[0][ks]);
+        mfma32_qk_first(s[kb][1], a, qf[1][ks]);
+      } else {
+        mfma32_qk(s[kb][0], a, qf[0][ks]);
+        mfma32_qk(s[kb][1], a, qf[1][ks]);
+      }
     }
+  }
+  qk_result_guard(s);
+}
+
+// Set element r of s to -inf when off(r) >= lim, off(r) = kb*32 + (r/4)*8 + r%4 being the key's
+// offset inside the tile minus 4*(lane/32).  Pure VGPR arithmetic (shift mask + bitfield insert):
+// a compare per element would park 64 lane masks in SGPRs.
+__device__ __forceinline__ void mask_block(f32x16& s, int kb, int lim) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+    const int m = (lim - 1 - off) >> 31;   // all ones when off >= lim
+    float out;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(out) : "v"(m), "v"(-INFINITY), "v"(s[r]));
+    s[r] = out;
   }
 }
 
@@ -165,6 +212,42 @@ __device__ __forceinline__ bf16x8 p_operand(const f32x16& p, int c) {
   return out;
 }
 
+// MFMA accumulating in AGPRs.  The P.V accumulator O (128 registers per lane at head_dim 128) is
+// kept in the accumulation registers so that the score tiles S(j), S(j+1) and P(j) fit in the
+// VGPRs beside it; the builtin would put every accumulator in one register class.  The leading
+// s_nop covers the VALU-write -> MFMA-read wait states (the operands are produced by VALU); reads
+// of the accumulator by VALU code must be preceded by agpr_read_guard(o).
+__device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Wait states between an MFMA writing the accumulator O and VALU code reading or rewriting it.  The
+// asm takes every accumulator as an in/out operand, so the compiler can place it neither before the
+// last MFMA that writes O nor after the first instruction that reads it.
+template <int D>
+__device__ __forceinline__ void agpr_read_guard(f32x16 (&o)[D / 32][2]) {
+  if constexpr (D == 128) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[2][0]),
+                   "+a"(o[2][1]), "+a"(o[3][0]), "+a"(o[3][1]));
+  } else {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[1][0]), "+a"(o[1][1]));
+  }
+}
+
+// Wait states between VALU code rewriting O and the next MFMA reading it as the accumulator input.
+template <int D>
+__device__ __forceinline__ void agpr_write_guard(f32x16 (&o)[D / 32][2]) {
+  if constexpr (D == 128) {
+    asm volatile("s_nop 4"
+                 : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[2][0]),
+                   "+a"(o[2][1]), "+a"(o[3][0]), "+a"(o[3][1]));
+  } else {
+    asm volatile("s_nop 4" : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[1][0]), "+a"(o[1][1]));
+  }
+}
+
 // O^T[d][q] += V^T . P^T over one 64-key tile; o[db][qb] is the 32x32 block d 32*db.., queries
 // 32*qb..; pb[kb][c][qb] from p_operand.
 template <int D>
@@ -185,8 +268,8 @@ __device__ __forceinline__ void pv_tile(const char* ldsV, const bf16x8 (&pb)[2][
             (lds_i16x4*)(ldsV + tile_offset<D>(row + 8, col)));
         const bf16x8 a = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[db][0] = mfma32(a, pb[kb][c][0], o[db][0]);
-        o[db][1] = mfma32(a, pb[kb][c][1], o[db][1]);
+        mfma32_agpr(o[db][0], a, pb[kb][c][0]);
+        mfma32_agpr(o[db][1], a, pb[kb][c][1]);
       }
     }
   }
