@@ -68,17 +68,27 @@ struct Dma {
   // Copy a 64-row tile into the LDS tile at `lds` (swizzled layout of tile_core.h).  Lane l of
   // instruction i lands at byte 1024*(wave*kPerWave + i) + 16*l, i.e. row r, physical chunk p; it
   // fetches logical chunk p ^ f(r), so logical chunk c of row r ends at physical c ^ f(r).
+  //
+  // Issued from inline asm: the compiler, seeing an LDS-writing load it cannot disambiguate,
+  // would otherwise wait for every outstanding copy (vmcnt(0)) before each later LDS read and
+  // drain the prefetches.  The explicit s_waitcnt vmcnt + barrier pairs in the loop are what
+  // order these copies against the reads.  M0 carries the LDS destination (no other use of M0
+  // remains in these kernels).
   static __device__ __forceinline__ void copy(char* lds, const __bf16* base, int bytes,
                                               int stride_b, int wave, int lane) {
     const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+    const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int inst = wave * kPerWave + i;
       const int row = inst * kRowsPerInst + lane / kChunksPerRow;
       const int chunk = chunk_swizzle<D>(row, lane % kChunksPerRow);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (__attribute__((address_space(3))) void*)(lds + inst * 1024), 16,
-          row * stride_b + chunk * 16, 0, 0, 0);
+      const unsigned dst = lds0 + inst * 1024;
+      const int voff = row * stride_b + chunk * 16;
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :
+                   : "s"(dst), "v"(voff), "s"(rsrc)
+                   : "memory", "m0");
     }
   }
 };
@@ -137,42 +147,49 @@ __device__ __forceinline__ void softmax_pv(const Pol& pol, int step, const f32x1
   if constexpr (Pol::kWeighted) weighted = pol.weighted(step);
 
   const int g = lane >> 4, j = lane & 15, h = lane >> 5;
+  // V^T operands of chunk n (16 keys: kb = n/2, c = n%2) for each 32-wide d block: two transpose
+  // reads each, issued one chunk ahead of the MFMAs that consume them.
+  auto vt = [&](int n, bf16x8 (&a)[D / 32]) {
+    const int kb = n >> 1, c = n & 1;
+    const int row = kb * 32 + c * 16 + 4 * h + (j >> 2);
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = db * 32 + 16 * (g & 1) + 4 * (j & 3);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(ldsV + tile_offset<D>(row, col)));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(ldsV + tile_offset<D>(row + 8, col)));
+      a[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  bf16x8 va[2][D / 32];
+  vt(0, va[0]);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      bf16x8 pb[2];
+  for (int n = 0; n < 4; ++n) {
+    const int kb = n >> 1, c = n & 1;
+    bf16x8 pb[2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float rs = 0.f;
+    for (int qb = 0; qb < 2; ++qb) {
+      float rs = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * c + e;
-          float p = __builtin_amdgcn_exp2f(s[kb][qb][r] * c32 - muse[qb]);
-          if constexpr (Pol::kFilter) p = ((ts.kbits[qb] >> (kb * 16 + r)) & 1u) ? p : 0.f;
-          if constexpr (Pol::kWeighted) {
-            rs += weighted ? p * pol.weight(step, kb, r, lane) : p;
-          } else {
-            rs += p;
-          }
-          pb[qb][e] = (__bf16)p;
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * c + e;
+        float p = __builtin_amdgcn_exp2f(s[kb][qb][r] * c32 - muse[qb]);
+        if constexpr (Pol::kFilter) p = ((ts.kbits[qb] >> (kb * 16 + r)) & 1u) ? p : 0.f;
+        if constexpr (Pol::kWeighted) {
+          rs += weighted ? p * pol.weight(step, kb, r, lane) : p;
+        } else {
+          rs += p;
         }
-        l[qb] += rs;
+        pb[qb][e] = (__bf16)p;
       }
-      // V^T operand of these 16 keys for each 32-wide d block (transpose reads), then MFMAs
-      const int row = kb * 32 + c * 16 + 4 * h + (j >> 2);
+      l[qb] += rs;
+    }
+    if (n + 1 < 4) vt(n + 1, va[(n + 1) & 1]);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int col = db * 32 + 16 * (g & 1) + 4 * (j & 3);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(ldsV + tile_offset<D>(row, col)));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(ldsV + tile_offset<D>(row + 8, col)));
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        mfma32_agpr(o[db][0], a, pb[0]);
-        mfma32_agpr(o[db][1], a, pb[1]);
-      }
+    for (int db = 0; db < D / 32; ++db) {
+      mfma32_agpr(o[db][0], va[n & 1][db], pb[0]);
+      mfma32_agpr(o[db][1], va[n & 1][db], pb[1]);
     }
   }
 }

@@ -125,11 +125,13 @@ __device__ __forceinline__ void park_q_in_agprs(bf16x8 (&qf)[2][D / 16]) {
     for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+a"(qf[qb][ks]));
 }
 
+// The MFMA asm statements are volatile with a memory clobber: LDS reads stay where the code puts
+// them relative to the MFMAs, which is how the operand prefetches below are scheduled.
 __device__ __forceinline__ void mfma32_qk_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b) : "memory");
 }
 __device__ __forceinline__ void mfma32_qk(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b) : "memory");
 }
 // Wait states between the QK MFMAs writing the scores and VALU code reading them (a 32x32x16 MFMA
 // has 8 passes; 20 wait states cover it with margin).  Tied to the score registers so that it sits
@@ -141,24 +143,34 @@ __device__ __forceinline__ void qk_result_guard(f32x16 (&s)[2][2]) {
 
 // S^T for one 64-key tile: s[kb][qb] is the 32x32 block keys 32*kb.., queries 32*qb..
 // Element r of lane l: key 32*kb + (r/4)*8 + 4*(l/32) + r%4, query 32*qb + l%32.
+// S^T for one 64-key tile: s[kb][qb] is the 32x32 block keys 32*kb.., queries 32*qb..
+// Element r of lane l: key 32*kb + (r/4)*8 + 4*(l/32) + r%4, query 32*qb + l%32.
+// K fragments are read from LDS kPrefetch steps ahead of the MFMAs that use them.
 template <int D>
 __device__ __forceinline__ void qk_tile(const char* ldsK, const bf16x8 (&qf)[2][D / 16],
                                         f32x16 (&s)[2][2], int lane) {
+  constexpr int KS = D / 16;        // 16-wide k steps per 32-key block
+  constexpr int NF = 2 * KS;        // fragments per tile
+  constexpr int kPrefetch = 4;
   const int h = lane >> 5, r32 = lane & 31;
+  auto frag = [&](int i) {
+    const int kb = i / KS, ks = i % KS, row = kb * 32 + r32;
+    return *reinterpret_cast<const bf16x8*>(ldsK + row * (D * 2) +
+                                            chunk_swizzle<D>(row, 2 * ks + h) * 16);
+  };
+  bf16x8 f[NF];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int row = kb * 32 + r32;
+  for (int i = 0; i < kPrefetch; ++i) f[i] = frag(i);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-          ldsK + row * (D * 2) + chunk_swizzle<D>(row, 2 * ks + h) * 16);
-      if (ks == 0) {
-        mfma32_qk_first(s[kb][0], a, qf[0][ks]);
-        mfma32_qk_first(s[kb][1], a, qf[1][ks]);
-      } else {
-        mfma32_qk(s[kb][0], a, qf[0][ks]);
-        mfma32_qk(s[kb][1], a, qf[1][ks]);
-      }
+  for (int i = 0; i < NF; ++i) {
+    if (i + kPrefetch < NF) f[i + kPrefetch] = frag(i + kPrefetch);
+    const int kb = i / KS, ks = i % KS;
+    if (ks == 0) {
+      mfma32_qk_first(s[kb][0], f[i], qf[0][ks]);
+      mfma32_qk_first(s[kb][1], f[i], qf[1][ks]);
+    } else {
+      mfma32_qk(s[kb][0], f[i], qf[0][ks]);
+      mfma32_qk(s[kb][1], f[i], qf[1][ks]);
     }
   }
   qk_result_guard(s);
@@ -218,7 +230,8 @@ __device__ __forceinline__ bf16x8 p_operand(const f32x16& p, int c) {
 // s_nop covers the VALU-write -> MFMA-read wait states (the operands are produced by VALU); reads
 // of the accumulator by VALU code must be preceded by agpr_read_guard(o).
 __device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+               : "+a"(acc) : "v"(a), "v"(b) : "memory");
 }
 
 // Wait states between an MFMA writing the accumulator O and VALU code reading or rewriting it.  The
