@@ -120,20 +120,26 @@ def source_digest(paths):
 
 
 SKIP_SOURCES = ["sparse_attention_flash_amd/csrc/skip_softmax.hip",
-                "sparse_attention_flash_amd/csrc/tile_core.h"]
+                "sparse_attention_flash_amd/csrc/tile_core.h",
+                "sparse_attention_flash_amd/csrc/mainloop.h",
+                "sparse_attention_flash_amd/csrc/kernels.h"]
 
 
-def measured_traffic(kernel_key, per_launch_algorithmic):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
-    current kernel source (else None)."""
-    path = os.path.join(PROFILES, "traffic.json")
+def measured_traffic(summary_name):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, each scaled by the plain-copy factor) from
+    the committed rocprofv3 summary, if it was taken on the current kernel source, else None."""
+    path = os.path.join(PROFILES, summary_name)
     if not os.path.exists(path):
         return None
+    fields = {}
     with open(path) as f:
-        rec = json.load(f).get(kernel_key)
-    if not rec or rec.get("source_digest") != source_digest(SKIP_SOURCES):
+        for line in f:
+            key, sep, val = line.partition(":")
+            if sep and key in ("hbm_bytes_per_launch", "source_digest"):
+                fields[key] = val.strip()
+    if fields.get("source_digest") != source_digest(SKIP_SOURCES):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return float(fields["hbm_bytes_per_launch"]) if "hbm_bytes_per_launch" in fields else None
 
 
 # ------------------------------------------------------------------------------------------------
@@ -339,7 +345,7 @@ def main():
                    "lambda": lam, "log2_lambda": log2_lam},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("skip_softmax_video_dit_s32760", computed)},
+                     "traffic": measured_traffic("skip_softmax_video_dit_s32760.txt")},
         "dense_equiv_tflops": round(dense / (ms * 1e-3) / 1e12, 2),
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "tile_sparsity": round(float(sparsity), 4),
