@@ -1,6 +1,6 @@
 // mainloop.h -- the pipelined key-tile loop shared by the skip-softmax, N:M and proxy kernels.
 //
-// One workgroup of NW wavefronts owns NW*64 query rows and walks a sequence of 64-key tiles
+// One workgroup of NW wavefronts, each owning QB blocks of 32 query rows, walks a sequence of 64-key tiles
 // ("steps") given by a policy object.  K and V tiles are copied HBM/L2 -> LDS with buffer loads
 // that write LDS directly (no staging registers), double-buffered.  Scores run two tiles ahead of
 // the softmax, so every tile is decided one full iteration before its V tile is needed:
@@ -29,6 +29,12 @@
 namespace sa {
 
 constexpr float kRescaleSlack = 8.f;
+
+// Query blocks of 32 rows per wavefront.  With one block a wave's registers (O 64, Q^T 32, two score
+// tiles 64, operands) fit in 256, so two waves share each SIMD; with two they need the whole file.
+constexpr int kQueryBlocksPerWave = 1;
+template <int QB>
+constexpr int kWavesPerSimd = QB == 1 ? 2 : 1;
 
 template <int D, int NW>
 struct Smem {
@@ -63,11 +69,32 @@ struct Dma {
   static constexpr int kPerWave = kTileBytes / 1024 / NW;   // 1 KiB per wave-wide instruction
   static constexpr int kRowsPerInst = 1024 / (D * 2);
   static constexpr int kChunksPerRow = D / 8;
+  static constexpr int kPeriod = D == 128 ? 16 : 8;          // rows after which chunk_swizzle repeats
+  static constexpr int kStepRows = NW * kRowsPerInst;        // rows between a wave's instructions
+  static constexpr int kClasses = kStepRows >= kPeriod ? 1 : kPeriod / kStepRows;
   static_assert(kPerWave >= 1 && kTileBytes % (1024 * NW) == 0, "tile must split over the waves");
+  static_assert(kPerWave % kClasses == 0 && (kClasses * kStepRows) % kPeriod == 0, "swizzle period");
 
-  // Copy a 64-row tile into the LDS tile at `lds` (swizzled layout of tile_core.h).  Lane l of
-  // instruction i lands at byte 1024*(wave*kPerWave + i) + 16*l, i.e. row r, physical chunk p; it
-  // fetches logical chunk p ^ f(r), so logical chunk c of row r ends at physical c ^ f(r).
+  // Instruction i of wave w fills rows (w + i*NW)*kRowsPerInst + lane/kChunksPerRow.  Rows that are
+  // kClasses*kStepRows apart share their chunk permutation, so a lane's byte offset inside the
+  // tile is off[i % kClasses] plus a uniform row shift that goes into the buffer resource base.
+  // Lane l of an instruction lands at byte 1024*(w + i*NW) + 16*l, i.e. row r, physical chunk p;
+  // it fetches logical chunk p ^ f(r), so logical chunk c of row r ends at physical c ^ f(r).
+  struct LaneOffsets {
+    int off[kClasses];
+  };
+  static __device__ __forceinline__ LaneOffsets lane_offsets(int stride_b, int wave, int lane) {
+    LaneOffsets lo;
+#pragma unroll
+    for (int c = 0; c < kClasses; ++c) {
+      const int row = wave * kRowsPerInst + c * kStepRows + lane / kChunksPerRow;
+      lo.off[c] = row * stride_b + chunk_swizzle<D>(row, lane % kChunksPerRow) * 16;
+    }
+    return lo;
+  }
+
+  // Copy a 64-row tile whose first row starts at `base` (`bytes` valid bytes from there; rows past
+  // them arrive as zeros) into the LDS tile at `lds`.
   //
   // Issued from inline asm: the compiler, seeing an LDS-writing load it cannot disambiguate,
   // would otherwise wait for every outstanding copy (vmcnt(0)) before each later LDS read and
@@ -75,27 +102,26 @@ struct Dma {
   // order these copies against the reads.  M0 carries the LDS destination (no other use of M0
   // remains in these kernels).
   static __device__ __forceinline__ void copy(char* lds, const __bf16* base, int bytes,
-                                              int stride_b, int wave, int lane) {
-    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+                                              int stride_b, const LaneOffsets& lo, int wave) {
     const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
-      const int inst = wave * kPerWave + i;
-      const int row = inst * kRowsPerInst + lane / kChunksPerRow;
-      const int chunk = chunk_swizzle<D>(row, lane % kChunksPerRow);
-      const unsigned dst = lds0 + inst * 1024;
-      const int voff = row * stride_b + chunk * 16;
+      const int shift = (i / kClasses) * kClasses * kStepRows * stride_b;   // uniform
+      const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((const char*)base + shift), (short)0, max(0, bytes - shift), 0x00020000);
+      const unsigned dst = lds0 + (wave + i * NW) * 1024;
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                    :
-                   : "s"(dst), "v"(voff), "s"(rsrc)
+                   : "s"(dst), "v"(lo.off[i % kClasses]), "s"(rsrc)
                    : "memory", "m0");
     }
   }
 };
 
-__device__ __forceinline__ void tile_row_max(const f32x16 (&s)[2][2], float c32, float (&M)[2]) {
+template <int QB>
+__device__ __forceinline__ void tile_row_max(const f32x16 (&s)[2][QB], float c32, float (&M)[QB]) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -106,43 +132,43 @@ __device__ __forceinline__ void tile_row_max(const f32x16 (&s)[2][2], float c32,
 }
 
 // Per-tile state: row maxima (log2 domain), N:M keep bits, decision.
+template <int QB>
 struct TileState {
-  float M[2];
-  uint32_t kbits[2];
+  float M[QB];
+  uint32_t kbits[QB];
   bool keep;
 };
 
 // Softmax of a kept tile fused with its P.V product.  For each 16-key chunk: exponentials of the
-// chunk (VALU), then the 8 MFMAs that consume them, so the VALU work of one chunk overlaps the
-// MFMAs of the previous one.  keep bits (N:M) zero dropped keys; Pol::weight (proxy) scales each
-// key's row-sum term.
-template <int D, class Pol>
-__device__ __forceinline__ void softmax_pv(const Pol& pol, int step, const f32x16 (&s)[2][2],
-                                           const TileState& ts, float (&mref)[2], float (&l)[2],
-                                           f32x16 (&o)[D / 32][2], const char* ldsV, float c32,
-                                           int lane) {
+// chunk (VALU), then the MFMAs that consume them, so the VALU work of one chunk overlaps the MFMAs
+// of the previous one.  keep bits (N:M) zero dropped keys; Pol::weight (proxy) scales each key's
+// row-sum term.  The row sum adds the fp32 weights (before their rounding to bf16 for P.V), which
+// keeps the LSE at fp32 accuracy.
+template <int D, int QB, class Pol>
+__device__ __forceinline__ void softmax_pv(const Pol& pol, int step, const f32x16 (&s)[2][QB],
+                                           const TileState<QB>& ts, float (&mref)[QB],
+                                           float (&l)[QB], f32x16 (&o)[D / 32][QB],
+                                           const char* ldsV, float c32, int lane) {
   bool need = false;
-  float cand[2];
+  float cand[QB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     cand[qb] = fmaxf(mref[qb], ts.M[qb]);
     need |= cand[qb] > mref[qb] + kRescaleSlack;   // also true when mref = -inf, M finite
   }
   if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
-    agpr_read_guard<D>(o);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       const float alpha = mref[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref[qb] - cand[qb]);
       l[qb] *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db][qb] *= alpha;
       mref[qb] = cand[qb];
     }
-    agpr_write_guard<D>(o);
   }
-  float muse[2];
+  float muse[QB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) muse[qb] = mref[qb] == -INFINITY ? 0.f : mref[qb];
+  for (int qb = 0; qb < QB; ++qb) muse[qb] = mref[qb] == -INFINITY ? 0.f : mref[qb];
   bool weighted = false;
   if constexpr (Pol::kWeighted) weighted = pol.weighted(step);
 
@@ -167,9 +193,9 @@ __device__ __forceinline__ void softmax_pv(const Pol& pol, int step, const f32x1
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int kb = n >> 1, c = n & 1;
-    bf16x8 pb[2];
+    bf16x8 pb[QB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       float rs = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -187,58 +213,60 @@ __device__ __forceinline__ void softmax_pv(const Pol& pol, int step, const f32x1
     }
     if (n + 1 < 4) vt(n + 1, va[(n + 1) & 1]);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      mfma32_agpr(o[db][0], va[n & 1][db], pb[0]);
-      mfma32_agpr(o[db][1], va[n & 1][db], pb[1]);
-    }
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma32(va[n & 1][db], pb[qb], o[db][qb]);
   }
 }
 
-// The step loop.  Pol provides:
+// The step loop.  Pol provides (arrays indexed by the wave's 32-row query blocks qb < QB):
 //   int steps() const;  TileSrc src(int step) const;
-//   void mask(int step, f32x16 (&s)[2][2], int lane) const;        -inf for masked keys
+//   void mask(int step, f32x16 (&s)[2][QB], int lane) const;        -inf for masked keys
 //   static constexpr bool kDecide, kFilter, kWeighted;
-//   bool negligible(const float (&M)[2], const float (&mt)[2], int lane) const;   [kDecide]
-//   void filter(int step, const f32x16 (&s)[2][2], uint32_t (&bits)[2], int lane) const; [kFilter]
+//   bool negligible(const float (&M)[QB], const float (&mt)[QB], int lane) const;   [kDecide]
+//   void filter(int step, const f32x16 (&s)[2][QB], uint32_t (&bits)[QB], int lane) const; [kFilter]
 //   bool weighted(int step) const; float weight(int step, int kb, int r, int lane) const; [kWeighted]
-//   void record(int step, bool keep, const float (&M)[2], int wave, int lane, int tid);
-// On return o, mref and l hold the unnormalised accumulator (AGPRs), exponent reference and
-// row-sum partials of this lane (l still to be summed over the two lane halves).
-template <int D, int NW, class Pol>
+//   void record(int step, bool keep, const float (&M)[QB], int wave, int lane, int tid);
+// On return o, mref and l hold the unnormalised accumulator, exponent reference and row-sum
+// partials of this lane (l still to be summed over the two lane halves).
+template <int D, int NW, int QB, class Pol>
 struct Mainloop {
   using DmaT = Dma<D, NW>;
+  using TS = TileState<QB>;
   static constexpr int kN = DmaT::kPerWave;   // loads per tile per lane
 
   Pol& pol;
   Smem<D, NW>& sm;
-  const bf16x8 (&qf)[2][D / 16];
-  f32x16 (&o)[D / 32][2];
-  float (&mref)[2];
-  float (&l)[2];
+  typename DmaT::LaneOffsets klo, vlo;
+  const bf16x8 (&qf)[QB][D / 16];
+  f32x16 (&o)[D / 32][QB];
+  float (&mref)[QB];
+  float (&l)[QB];
   float c32;
   int wave, lane, tid, n;
-  float mt[2] = {-INFINITY, -INFINITY};   // running max of kept tiles' maxima (decision state)
+  float mt[QB];   // running max of kept tiles' maxima (decision state)
 
   __device__ __forceinline__ void issue_k(int step) {
     const TileSrc t = pol.src(step);
-    DmaT::copy(sm.k[step & 1], t.k, t.k_bytes, t.k_stride_b, wave, lane);
+    DmaT::copy(sm.k[step & 1], t.k, t.k_bytes, t.k_stride_b, klo, wave);
   }
   __device__ __forceinline__ void issue_v(int step) {
     const TileSrc t = pol.src(step);
-    DmaT::copy(sm.v[step & 1], t.v, t.v_bytes, t.v_stride_b, wave, lane);
+    DmaT::copy(sm.v[step & 1], t.v, t.v_bytes, t.v_stride_b, vlo, wave);
   }
 
   // S(step) from the K tile in LDS, masked, with its row maxima and N:M bits.
-  __device__ __forceinline__ void scores(int step, f32x16 (&s)[2][2], TileState& ts) {
-    qk_tile<D>(sm.k[step & 1], qf, s, lane);
+  __device__ __forceinline__ void scores(int step, f32x16 (&s)[2][QB], TS& ts) {
+    qk_tile<D, QB>(sm.k[step & 1], qf, s, lane);
     pol.mask(step, s, lane);
-    tile_row_max(s, c32, ts.M);
-    ts.kbits[0] = ts.kbits[1] = ~0u;
+    tile_row_max<QB>(s, c32, ts.M);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) ts.kbits[qb] = ~0u;
     if constexpr (Pol::kFilter) pol.filter(step, s, ts.kbits, lane);
   }
 
   // Vote through LDS; one barrier.  A kept tile raises the decision max mt at once.
-  __device__ __forceinline__ void decide(int step, TileState& ts) {
+  __device__ __forceinline__ void decide(int step, TS& ts) {
     if constexpr (Pol::kDecide) {
       const bool wave_keep = __builtin_amdgcn_ballot_w64(!pol.negligible(ts.M, mt, lane)) != 0ull;
       if (lane == 0) sm.vote[step & 1][wave] = wave_keep ? 1 : 0;
@@ -252,22 +280,21 @@ struct Mainloop {
       ts.keep = any != 0;
     }
     if (ts.keep) {
-      mt[0] = fmaxf(mt[0], ts.M[0]);
-      mt[1] = fmaxf(mt[1], ts.M[1]);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) mt[qb] = fmaxf(mt[qb], ts.M[qb]);
     }
     pol.record(step, ts.keep, ts.M, wave, lane, tid);
   }
 
   // iteration j: S(j) in sa (state ta), S(j+1) decided (state tb); S(j+2) is written into sa.
-  __device__ __forceinline__ void iteration(int j, f32x16 (&sa)[2][2], TileState& ta,
-                                            const TileState& tb) {
+  __device__ __forceinline__ void iteration(int j, f32x16 (&sa)[2][QB], TS& ta, const TS& tb) {
     // 1: V(j) and K(j+2) landed; V(j+1), the newest load, may still be in flight
     if (tb.keep) wait_vmcnt<kN>(); else wait_vmcnt<0>();
     lds_barrier();
     // 2: prefetch K(j+3) into the buffer K(j+1) used
     if (j + 3 < n) issue_k(j + 3);
     // 3: softmax(j) fused with O += P(j) V(j)
-    if (ta.keep) softmax_pv<D>(pol, j, sa, ta, mref, l, o, sm.v[j & 1], c32, lane);
+    if (ta.keep) softmax_pv<D, QB>(pol, j, sa, ta, mref, l, o, sm.v[j & 1], c32, lane);
     // 4-6: S(j+2), its vote, its V tile
     if (j + 2 < n) {
       scores(j + 2, sa, ta);
@@ -279,9 +306,16 @@ struct Mainloop {
   }
 
   __device__ __forceinline__ void run() {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mt[qb] = -INFINITY;
     if (n <= 0) return;
-    f32x16 sa[2][2], sb[2][2];
-    TileState ta, tb;
+    {
+      const TileSrc t = pol.src(0);
+      klo = DmaT::lane_offsets(t.k_stride_b, wave, lane);
+      vlo = DmaT::lane_offsets(t.v_stride_b, wave, lane);
+    }
+    f32x16 sa[2][QB], sb[2][QB];
+    TS ta, tb;
     // prologue: K(0), K(1); S(0), keep(0), V(0); K(2); S(1), keep(1), V(1)
     issue_k(0);
     if (n > 1) issue_k(1);
@@ -309,13 +343,13 @@ struct Mainloop {
   }
 };
 
-template <int D, int NW, class Pol>
+template <int D, int NW, int QB, class Pol>
 __device__ __forceinline__ void run_mainloop(Pol& pol, Smem<D, NW>& sm,
-                                             const bf16x8 (&qf)[2][D / 16],
-                                             f32x16 (&o)[D / 32][2], float (&mref)[2],
-                                             float (&l)[2], float c32, int wave, int lane,
+                                             const bf16x8 (&qf)[QB][D / 16],
+                                             f32x16 (&o)[D / 32][QB], float (&mref)[QB],
+                                             float (&l)[QB], float c32, int wave, int lane,
                                              int tid) {
-  Mainloop<D, NW, Pol> ml{pol, sm, qf, o, mref, l, c32, wave, lane, tid, pol.steps()};
+  Mainloop<D, NW, QB, Pol> ml{pol, sm, {}, {}, qf, o, mref, l, c32, wave, lane, tid, pol.steps()};
   ml.run();
 }
 

@@ -55,9 +55,10 @@ __device__ __forceinline__ void group_ranks(const float (&own)[4], const float (
   }
 }
 
-template <int D, int NW, int M>
+template <int D, int NW, int QB, int M>
 struct NmPolicy {
   static constexpr bool kDecide = false, kFilter = true, kWeighted = false;
+  static constexpr int RW = 32 * QB;   // rows per wave
   const __bf16* kslab;
   const __bf16* vslab;
   int k_stride_b, v_stride_b, k_bytes, v_bytes;
@@ -75,12 +76,12 @@ struct NmPolicy {
                    k_stride_b, v_stride_b};
   }
 
-  __device__ __forceinline__ void mask(int j, f32x16 (&s)[2][2], int lane) const {
+  __device__ __forceinline__ void mask(int j, f32x16 (&s)[2][QB], int lane) const {
     const int k0 = j * kKeysPerTile;
     if (!((k0 + kKeysPerTile > Sk) || (causal && k0 + kKeysPerTile - 1 > wrow0))) return;
     const int klim = Sk - k0 - 4 * h;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       int lim = klim;
       if (causal) lim = min(lim, wrow0 + qb * 32 + r32 - k0 - 4 * h + 1);
 #pragma unroll
@@ -91,14 +92,14 @@ struct NmPolicy {
   // keep bit (kb*16 + r) of bits[qb]: key not masked and (dense, or top-n of its group).  All
   // per-element tests are sign-bit arithmetic; the sink/recent windows and masked keys only occur
   // on a few tiles per row, tested once per tile.
-  __device__ __forceinline__ void filter(int j, const f32x16 (&s)[2][2], uint32_t (&bits)[2],
+  __device__ __forceinline__ void filter(int j, const f32x16 (&s)[2][QB], uint32_t (&bits)[QB],
                                          int lane) const {
     const int k0 = j * kKeysPerTile;
     const bool any_masked = (k0 + kKeysPerTile > Sk) || (causal && k0 + kKeysPerTile - 1 > wrow0);
     const bool any_dense = k0 < sink ||
-        (recent > 0 && k0 <= wrow0 + kRowsPerWave - 1 && k0 + kKeysPerTile - 1 > wrow0 - recent);
+        (recent > 0 && k0 <= wrow0 + RW - 1 && k0 + kKeysPerTile - 1 > wrow0 - recent);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       const int row = wrow0 + qb * 32 + r32;
       uint32_t kb_bits = 0u;
 #pragma unroll
@@ -148,7 +149,7 @@ struct NmPolicy {
 
   // debug exports of one query row: keep-bit words and raw scores
   __device__ __forceinline__ void export_row(int k0, int row, int qb, uint32_t kb_bits,
-                                             const f32x16 (&s)[2][2], int lane) const {
+                                             const f32x16 (&s)[2][QB], int lane) const {
     // lanes l and l^32 hold the same row: both stay active through the swap
     const int64_t rbase = row_base + row;
 #pragma unroll
@@ -172,15 +173,17 @@ struct NmPolicy {
     }
   }
 
-  __device__ __forceinline__ bool negligible(const float (&)[2], const float (&)[2], int) const {
+  __device__ __forceinline__ bool negligible(const float (&)[QB], const float (&)[QB], int) const {
     return false;
   }
-  __device__ __forceinline__ void record(int, bool, const float (&)[2], int, int, int) {}
+  __device__ __forceinline__ void record(int, bool, const float (&)[QB], int, int, int) {}
 };
 
-template <int D, int NW, int M>
-__global__ __launch_bounds__(NW * 64) void nm_softmax_kernel(NmArgs a) {
-  constexpr int BR = NW * kRowsPerWave;
+template <int D, int NW, int QB, int M>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<QB>)))
+void nm_softmax_kernel(NmArgs a) {
+  constexpr int RW = 32 * QB;
+  constexpr int BR = NW * RW;
   constexpr int NT = NW * 64;
   __shared__ __attribute__((aligned(1024))) Smem<D, NW> sm;
 
@@ -204,17 +207,16 @@ __global__ __launch_bounds__(NW * 64) void nm_softmax_kernel(NmArgs a) {
   const int hq = hk * G + gq;
 
   const int row0 = qt * BR;
-  const int wrow0 = row0 + wave * kRowsPerWave;
+  const int wrow0 = row0 + wave * RW;
   const int last_row = min(row0 + BR, g.Sq) - 1;
   const int nvis = g.causal ? min(nKT, last_row / kKeysPerTile + 1) : nKT;
   const int W = (g.Sk + 31) / 32;
 
   const auto qsrc = slab_rsrc((const __bf16*)g.q + b * g.qs[0] + hq * g.qs[2], g.qs[1], g.Sq, D);
-  bf16x8 qf[2][D / 16];
-  load_q_frags<D>(qf, qsrc, g.qs[1], wrow0, lane);
-  park_q_in_agprs<D>(qf);
+  bf16x8 qf[QB][D / 16];
+  load_q_frags<D, QB>(qf, qsrc, g.qs[1], wrow0, lane);
 
-  NmPolicy<D, NW, M> pol;
+  NmPolicy<D, NW, QB, M> pol;
   pol.kslab = (const __bf16*)g.k + b * g.ks[0] + hk * g.ks[2];
   pol.vslab = (const __bf16*)g.v + b * g.vs[0] + hk * g.vs[2];
   pol.k_stride_b = (int)(g.ks[1] * 2);
@@ -236,12 +238,16 @@ __global__ __launch_bounds__(NW * 64) void nm_softmax_kernel(NmArgs a) {
   pol.scores = a.scores;
   pol.row_base = ((int64_t)b * g.Hq + hq) * g.Sq;
 
-  f32x16 o[D / 32][2];
+  f32x16 o[D / 32][QB];
+  float mref[QB], l[QB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db][0] = o[db][1] = f32x16{};
-  float mref[2] = {-INFINITY, -INFINITY};
-  float l[2] = {0.f, 0.f};
-  run_mainloop<D, NW>(pol, sm, qf, o, mref, l, g.c32, wave, lane, tid);
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db][qb] = f32x16{};
+    mref[qb] = -INFINITY;
+    l[qb] = 0.f;
+  }
+  run_mainloop<D, NW, QB>(pol, sm, qf, o, mref, l, g.c32, wave, lane, tid);
 
   // keep-bit words and scores of tiles never visited (causal): zero / -inf
   if (a.keep_bits != nullptr) {
@@ -263,10 +269,9 @@ __global__ __launch_bounds__(NW * 64) void nm_softmax_kernel(NmArgs a) {
     }
   }
 
-  agpr_read_guard<D>(o);
-  float inv[2];
+  float inv[QB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float lt = half_sum(l[qb]);
     inv[qb] = lt > 0.f ? 1.f / lt : 0.f;
     const int row = wrow0 + qb * 32 + r32;
@@ -275,29 +280,31 @@ __global__ __launch_bounds__(NW * 64) void nm_softmax_kernel(NmArgs a) {
           lt > 0.f ? (mref[qb] + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
   }
   __bf16* op = (__bf16*)g.o + b * g.os[0] + (int64_t)wrow0 * g.os[1] + hq * g.os[2];
-  store_o<D>(op, g.os[1], g.Sq - wrow0, o, inv, lane);
+  store_o<D, QB>(op, g.os[1], g.Sq - wrow0, o, inv, lane);
 }
 
-template <int D, int NW, int M>
+template <int D, int NW, int QB, int M>
 hipError_t launch_t(const NmArgs& a, hipStream_t stream) {
-  constexpr int BR = NW * kRowsPerWave;
+  constexpr int BR = NW * 32 * QB;
   const int nQT = (a.g.Sq + BR - 1) / BR;
   const int total = a.g.B * a.g.Hq * nQT;
-  hipLaunchKernelGGL((nm_softmax_kernel<D, NW, M>), dim3(total), dim3(NW * 64), 0, stream, a);
+  hipLaunchKernelGGL((nm_softmax_kernel<D, NW, QB, M>), dim3(total), dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, int NW>
+template <int D, int NW, int QB>
 hipError_t launch_m(const NmArgs& a, hipStream_t stream) {
-  return a.m == 8 ? launch_t<D, NW, 8>(a, stream) : launch_t<D, NW, 4>(a, stream);
+  return a.m == 8 ? launch_t<D, NW, QB, 8>(a, stream) : launch_t<D, NW, QB, 4>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_nm_softmax(const NmArgs& a, hipStream_t stream) {
+  constexpr int QB = kQueryBlocksPerWave;
   const bool q128 = a.g.block_q == 128;
-  if (a.g.D == 128) return q128 ? launch_m<128, 2>(a, stream) : launch_m<128, 1>(a, stream);
-  return q128 ? launch_m<64, 2>(a, stream) : launch_m<64, 1>(a, stream);
+  if (a.g.D == 128)
+    return q128 ? launch_m<128, 4 / QB, QB>(a, stream) : launch_m<128, 2 / QB, QB>(a, stream);
+  return q128 ? launch_m<64, 4 / QB, QB>(a, stream) : launch_m<64, 2 / QB, QB>(a, stream);
 }
 
 }  // namespace sa

@@ -20,7 +20,7 @@ namespace sa {
 namespace {
 
 // Exact steps (pipelined main loop): the 64-key tiles of the exact blocks, in ascending order.
-template <int D, int NW>
+template <int D, int NW, int QB>
 struct ExactPolicy {
   static constexpr bool kDecide = false, kFilter = false, kWeighted = false;
   const __bf16* kslab;
@@ -44,26 +44,26 @@ struct ExactPolicy {
   }
 
   // keys past Sk exist only in the final partial block
-  __device__ __forceinline__ void mask(int step, f32x16 (&s)[2][2], int lane) const {
+  __device__ __forceinline__ void mask(int step, f32x16 (&s)[2][QB], int lane) const {
     const int k0 = first_key(step);
     if (k0 + kKeysPerTile <= Sk) return;
     const int lim = Sk - k0 - 4 * h;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      mask_block(s[kb][0], kb, lim);
-      mask_block(s[kb][1], kb, lim);
-    }
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) mask_block(s[kb][qb], kb, lim);
   }
 
-  __device__ __forceinline__ bool negligible(const float (&)[2], const float (&)[2], int) const {
+  __device__ __forceinline__ bool negligible(const float (&)[QB], const float (&)[QB], int) const {
     return false;
   }
-  __device__ __forceinline__ void filter(int, const f32x16 (&)[2][2], uint32_t (&)[2], int) const {}
-  __device__ __forceinline__ void record(int, bool, const float (&)[2], int, int, int) {}
+  __device__ __forceinline__ void filter(int, const f32x16 (&)[2][QB], uint32_t (&)[QB], int) const {}
+  __device__ __forceinline__ void record(int, bool, const float (&)[QB], int, int, int) {}
 };
 
 // Proxy tiles: 64 summary rows at a time; rows whose proxy_keep bit is clear (or past nKB) are
 // masked, and each kept row's row-sum term is weighted by its token mass c_j.
+template <int QB>
 struct SummaryPolicy {
   static constexpr bool kFilter = false, kWeighted = true;
   const uint32_t* keep;  // proxy_keep words of this query block
@@ -71,7 +71,7 @@ struct SummaryPolicy {
 
   __device__ __forceinline__ bool weighted(int) const { return true; }
 
-  __device__ __forceinline__ void mask(int t, f32x16 (&s)[2][2]) const {
+  __device__ __forceinline__ void mask(int t, f32x16 (&s)[2][QB]) const {
     const int r0 = t * kKeysPerTile;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -84,12 +84,9 @@ struct SummaryPolicy {
       const uint32_t lane_bits = bits >> (4 * h);   // element r holds bit (r/4)*8 + r%4 of these
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = (int)((lane_bits >> ((r >> 2) * 8 + (r & 3))) & 1u) - 1;   // -1: drop
-        float o0, o1;
-        asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(o0) : "v"(m), "v"(-INFINITY), "v"(s[kb][0][r]));
-        asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(o1) : "v"(m), "v"(-INFINITY), "v"(s[kb][1][r]));
-        s[kb][0][r] = o0;
-        s[kb][1][r] = o1;
+        const uint32_t m = ((lane_bits >> ((r >> 2) * 8 + (r & 3))) & 1u) - 1u;   // ~0: drop
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb][r] = select_neg_inf(s[kb][qb][r], m);
       }
     }
   }
@@ -101,9 +98,11 @@ struct SummaryPolicy {
   }
 };
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void proxy_kernel(ProxyArgs a) {
-  constexpr int BR = NW * kRowsPerWave;
+template <int D, int NW, int QB>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<QB>)))
+void proxy_kernel(ProxyArgs a) {
+  constexpr int RW = 32 * QB;
+  constexpr int BR = NW * RW;
   __shared__ __attribute__((aligned(1024))) Smem<D, NW> sm;
 
   const AttnGeom& g = a.g;
@@ -127,15 +126,14 @@ __global__ __launch_bounds__(NW * 64) void proxy_kernel(ProxyArgs a) {
   const int hq = hk * G + gq;
 
   const int row0 = qb_blk * BR;
-  const int wrow0 = row0 + wave * kRowsPerWave;
+  const int wrow0 = row0 + wave * RW;
   const int64_t route_row = ((int64_t)b * g.Hkv + hk) * nQB + qb_blk;
 
   const auto qsrc = slab_rsrc((const __bf16*)g.q + b * g.qs[0] + hq * g.qs[2], g.qs[1], g.Sq, D);
-  bf16x8 qf[2][D / 16];
-  load_q_frags<D>(qf, qsrc, g.qs[1], wrow0, lane);
-  park_q_in_agprs<D>(qf);
+  bf16x8 qf[QB][D / 16];
+  load_q_frags<D, QB>(qf, qsrc, g.qs[1], wrow0, lane);
 
-  ExactPolicy<D, NW> pol;
+  ExactPolicy<D, NW, QB> pol;
   pol.kslab = (const __bf16*)g.k + b * g.ks[0] + hk * g.ks[2];
   pol.vslab = (const __bf16*)g.v + b * g.vs[0] + hk * g.vs[2];
   pol.exact = a.exact_idx + route_row * nKB;
@@ -150,16 +148,20 @@ __global__ __launch_bounds__(NW * 64) void proxy_kernel(ProxyArgs a) {
   pol.n_exact = min(max(__builtin_amdgcn_readfirstlane(a.n_exact[route_row]), 0), nKB);
   pol.h = h;
 
-  f32x16 o[D / 32][2];
+  f32x16 o[D / 32][QB];
+  float mref[QB], l[QB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db][0] = o[db][1] = f32x16{};
-  float mref[2] = {-INFINITY, -INFINITY};
-  float l[2] = {0.f, 0.f};
-  run_mainloop<D, NW>(pol, sm, qf, o, mref, l, g.c32, wave, lane, tid);
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db][qb] = f32x16{};
+    mref[qb] = -INFINITY;
+    l[qb] = 0.f;
+  }
+  run_mainloop<D, NW, QB>(pol, sm, qf, o, mref, l, g.c32, wave, lane, tid);
 
   // proxy tiles: summaries as keys, one tile at a time
   if (a.use_proxy) {
-    SummaryPolicy sp;
+    SummaryPolicy<QB> sp;
     sp.keep = a.proxy_keep + route_row * Wd;
     sp.Bk = Bk;
     sp.nKB = nKB;
@@ -170,29 +172,30 @@ __global__ __launch_bounds__(NW * 64) void proxy_kernel(ProxyArgs a) {
     const __bf16* kmean = (const __bf16*)a.k_mean + sbase;
     const __bf16* vsum = (const __bf16*)a.v_sum + sbase;
     const int n_tiles = (nKB + kKeysPerTile - 1) / kKeysPerTile;
+    const auto slo = Dma<D, NW>::lane_offsets(D * 2, wave, lane);
     for (int t = 0; t < n_tiles; ++t) {
       const int r0 = t * kKeysPerTile;
       const int bytes = (nKB - r0) * D * 2;
       lds_barrier();   // every wave is done with the buffers the loop above (or tile t-1) used
-      Dma<D, NW>::copy(sm.k[0], kmean + (int64_t)r0 * D, bytes, D * 2, wave, lane);
-      Dma<D, NW>::copy(sm.v[0], vsum + (int64_t)r0 * D, bytes, D * 2, wave, lane);
+      Dma<D, NW>::copy(sm.k[0], kmean + (int64_t)r0 * D, bytes, D * 2, slo, wave);
+      Dma<D, NW>::copy(sm.v[0], vsum + (int64_t)r0 * D, bytes, D * 2, slo, wave);
       wait_vmcnt<0>();
       lds_barrier();
-      f32x16 s[2][2];
-      qk_tile<D>(sm.k[0], qf, s, lane);
+      f32x16 s[2][QB];
+      qk_tile<D, QB>(sm.k[0], qf, s, lane);
       sp.mask(t, s);
-      TileState ts;
-      tile_row_max(s, g.c32, ts.M);
-      ts.kbits[0] = ts.kbits[1] = ~0u;
+      TileState<QB> ts;
+      tile_row_max<QB>(s, g.c32, ts.M);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) ts.kbits[qb] = ~0u;
       ts.keep = true;
-      softmax_pv<D>(sp, t, s, ts, mref, l, o, sm.v[0], g.c32, lane);
+      softmax_pv<D, QB>(sp, t, s, ts, mref, l, o, sm.v[0], g.c32, lane);
     }
   }
 
-  agpr_read_guard<D>(o);
-  float inv[2];
+  float inv[QB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float lt = half_sum(l[qb]);
     inv[qb] = lt > 0.f ? 1.f / lt : 0.f;
     const int row = wrow0 + qb * 32 + r32;
@@ -201,24 +204,26 @@ __global__ __launch_bounds__(NW * 64) void proxy_kernel(ProxyArgs a) {
           lt > 0.f ? (mref[qb] + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
   }
   __bf16* op = (__bf16*)g.o + b * g.os[0] + (int64_t)wrow0 * g.os[1] + hq * g.os[2];
-  store_o<D>(op, g.os[1], g.Sq - wrow0, o, inv, lane);
+  store_o<D, QB>(op, g.os[1], g.Sq - wrow0, o, inv, lane);
 }
 
-template <int D, int NW>
+template <int D, int NW, int QB>
 hipError_t launch_t(const ProxyArgs& a, hipStream_t stream) {
-  constexpr int BR = NW * kRowsPerWave;
+  constexpr int BR = NW * 32 * QB;
   const int nQB = (a.g.Sq + BR - 1) / BR;
   const int total = a.g.B * a.g.Hq * nQB;
-  hipLaunchKernelGGL((proxy_kernel<D, NW>), dim3(total), dim3(NW * 64), 0, stream, a);
+  hipLaunchKernelGGL((proxy_kernel<D, NW, QB>), dim3(total), dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_proxy(const ProxyArgs& a, hipStream_t stream) {
+  constexpr int QB = kQueryBlocksPerWave;
   const bool q128 = a.g.block_q == 128;
-  if (a.g.D == 128) return q128 ? launch_t<128, 2>(a, stream) : launch_t<128, 1>(a, stream);
-  return q128 ? launch_t<64, 2>(a, stream) : launch_t<64, 1>(a, stream);
+  if (a.g.D == 128)
+    return q128 ? launch_t<128, 4 / QB, QB>(a, stream) : launch_t<128, 2 / QB, QB>(a, stream);
+  return q128 ? launch_t<64, 4 / QB, QB>(a, stream) : launch_t<64, 2 / QB, QB>(a, stream);
 }
 
 }  // namespace sa

@@ -8,7 +8,8 @@
 //     M_j[r] < fl32(m[r] + log2(lambda)),
 // m[r] being the fp32 running max of the tiles kept so far; a skipped tile leaves (m, l, O) alone.
 //
-// One workgroup = one (batch, query head, query tile of 64*NW rows); each wavefront owns 64 rows.
+// One workgroup = one (batch, query head, query tile of 32*QB*NW rows); each wavefront owns 32*QB
+// rows.
 // The pipelined loop (mainloop.h) computes S^T = K.Q^T on MFMA, masks, takes the row max (in-lane
 // plus one permlane32 swap), and each wavefront votes "some row not negligible" with a ballot; the
 // votes meet in LDS at the barrier that also publishes the previous V tile.  Only a kept tile has
@@ -19,10 +20,11 @@
 namespace sa {
 namespace {
 
-template <int D, int NW>
+template <int D, int NW, int QB>
 struct SkipPolicy {
   static constexpr bool kDecide = true, kFilter = false, kWeighted = false;
-  static constexpr int BR = NW * kRowsPerWave;
+  static constexpr int RW = 32 * QB;   // rows per wave
+  static constexpr int BR = NW * RW;
   const __bf16* kslab;
   const __bf16* vslab;
   int k_stride_b, v_stride_b, k_bytes, v_bytes;
@@ -43,12 +45,12 @@ struct SkipPolicy {
   }
 
   // key = k0 + 4*h + off(kb, r) with off a compile-time constant; masked when off >= lim
-  __device__ __forceinline__ void mask(int j, f32x16 (&s)[2][2], int lane) const {
+  __device__ __forceinline__ void mask(int j, f32x16 (&s)[2][QB], int lane) const {
     const int k0 = j * kKeysPerTile;
     if (!((k0 + kKeysPerTile > Sk) || (causal && k0 + kKeysPerTile - 1 > wrow0))) return;
     const int klim = Sk - k0 - 4 * h;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       int lim = klim;
       if (causal) lim = min(lim, wrow0 + qb * 32 + r32 - k0 - 4 * h + 1);
 #pragma unroll
@@ -57,34 +59,36 @@ struct SkipPolicy {
   }
 
   // true when every valid row this lane holds is negligible: M < fl32(m + log2(lambda))
-  __device__ __forceinline__ bool negligible(const float (&M)[2], const float (&mt)[2],
+  __device__ __forceinline__ bool negligible(const float (&M)[QB], const float (&mt)[QB],
                                              int lane) const {
     bool negl = true;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       const float thr = mt[qb] + L32;
       if (wrow0 + qb * 32 + r32 < Sq && !(M[qb] < thr)) negl = false;
     }
     return negl;
   }
 
-  __device__ __forceinline__ void record(int j, bool keep, const float (&M)[2], int wave,
+  __device__ __forceinline__ void record(int j, bool keep, const float (&M)[QB], int wave,
                                          int lane, int tid) {
     if (!keep) ++nskip;
     if (tid == 0 && tile_state != nullptr) tile_state[unit * nKT + j] = keep ? 0 : 1;
     if (rowmax != nullptr && h == 0) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        rowmax[(unit * nKT + j) * BR + wave * kRowsPerWave + qb * 32 + r32] = M[qb];
+      for (int qb = 0; qb < QB; ++qb)
+        rowmax[(unit * nKT + j) * BR + wave * RW + qb * 32 + r32] = M[qb];
     }
   }
 
-  __device__ __forceinline__ void filter(int, const f32x16 (&)[2][2], uint32_t (&)[2], int) const {}
+  __device__ __forceinline__ void filter(int, const f32x16 (&)[2][QB], uint32_t (&)[QB], int) const {}
 };
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void skip_softmax_kernel(SkipArgs a) {
-  constexpr int BR = NW * kRowsPerWave;
+template <int D, int NW, int QB>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<QB>)))
+void skip_softmax_kernel(SkipArgs a) {
+  constexpr int RW = 32 * QB;
+  constexpr int BR = NW * RW;
   constexpr int NT = NW * 64;
   __shared__ __attribute__((aligned(1024))) Smem<D, NW> sm;
 
@@ -111,17 +115,16 @@ __global__ __launch_bounds__(NW * 64) void skip_softmax_kernel(SkipArgs a) {
   const int hq = hk * G + gq;
 
   const int row0 = qt * BR;
-  const int wrow0 = row0 + wave * kRowsPerWave;
+  const int wrow0 = row0 + wave * RW;
   const int last_row = min(row0 + BR, g.Sq) - 1;
   const int nvis = g.causal ? min(nKT, last_row / kKeysPerTile + 1) : nKT;
 
   const __bf16* qslab = (const __bf16*)g.q + b * g.qs[0] + hq * g.qs[2];
   const auto qsrc = slab_rsrc(qslab, g.qs[1], g.Sq, D);
-  bf16x8 qf[2][D / 16];
-  load_q_frags<D>(qf, qsrc, g.qs[1], wrow0, lane);
-  park_q_in_agprs<D>(qf);
+  bf16x8 qf[QB][D / 16];
+  load_q_frags<D, QB>(qf, qsrc, g.qs[1], wrow0, lane);
 
-  SkipPolicy<D, NW> pol;
+  SkipPolicy<D, NW, QB> pol;
   pol.kslab = (const __bf16*)g.k + b * g.ks[0] + hk * g.ks[2];
   pol.vslab = (const __bf16*)g.v + b * g.vs[0] + hk * g.vs[2];
   pol.k_stride_b = (int)(g.ks[1] * 2);
@@ -142,18 +145,21 @@ __global__ __launch_bounds__(NW * 64) void skip_softmax_kernel(SkipArgs a) {
   pol.unit = ((int64_t)b * g.Hq + hq) * nQT + qt;
   pol.nskip = 0;
 
-  f32x16 o[D / 32][2];
+  f32x16 o[D / 32][QB];
+  float mref[QB], l[QB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db][0] = o[db][1] = f32x16{};
-  float mref[2] = {-INFINITY, -INFINITY};
-  float l[2] = {0.f, 0.f};
-  run_mainloop<D, NW>(pol, sm, qf, o, mref, l, g.c32, wave, lane, tid);
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db][qb] = f32x16{};
+    mref[qb] = -INFINITY;
+    l[qb] = 0.f;
+  }
+  run_mainloop<D, NW, QB>(pol, sm, qf, o, mref, l, g.c32, wave, lane, tid);
 
   // Epilogue: normalise, store O and the natural-log LSE.
-  agpr_read_guard<D>(o);
-  float inv[2];
+  float inv[QB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float lt = half_sum(l[qb]);
     inv[qb] = lt > 0.f ? 1.f / lt : 0.f;
     const int row = wrow0 + qb * 32 + r32;
@@ -162,7 +168,7 @@ __global__ __launch_bounds__(NW * 64) void skip_softmax_kernel(SkipArgs a) {
           lt > 0.f ? (mref[qb] + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
   }
   __bf16* op = (__bf16*)g.o + b * g.os[0] + (int64_t)wrow0 * g.os[1] + hq * g.os[2];
-  store_o<D>(op, g.os[1], g.Sq - wrow0, o, inv, lane);
+  store_o<D, QB>(op, g.os[1], g.Sq - wrow0, o, inv, lane);
 
   const int64_t unit = pol.unit;
   if (a.tile_state != nullptr)
@@ -176,21 +182,26 @@ __global__ __launch_bounds__(NW * 64) void skip_softmax_kernel(SkipArgs a) {
   }
 }
 
-template <int D, int NW>
+template <int D, int NW, int QB>
 hipError_t launch_t(const SkipArgs& a, hipStream_t stream) {
-  constexpr int BR = NW * kRowsPerWave;
+  constexpr int BR = NW * 32 * QB;
   const int nQT = (a.g.Sq + BR - 1) / BR;
   const int total = a.g.B * a.g.Hq * nQT;
-  hipLaunchKernelGGL((skip_softmax_kernel<D, NW>), dim3(total), dim3(NW * 64), 0, stream, a);
+  hipLaunchKernelGGL((skip_softmax_kernel<D, NW, QB>), dim3(total), dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Query tiles of block_q rows run as block_q/32 wavefronts of 32 rows each (kQueryBlocksPerWave =
+// 1): the per-wave state then fits in half the register file, so two workgroups share each CU and
+// one's MFMA work overlaps the other's softmax arithmetic.
 hipError_t launch_skip_softmax(const SkipArgs& a, hipStream_t stream) {
+  constexpr int QB = kQueryBlocksPerWave;
   const bool q128 = a.g.block_q == 128;
-  if (a.g.D == 128) return q128 ? launch_t<128, 2>(a, stream) : launch_t<128, 1>(a, stream);
-  return q128 ? launch_t<64, 2>(a, stream) : launch_t<64, 1>(a, stream);
+  if (a.g.D == 128)
+    return q128 ? launch_t<128, 4 / QB, QB>(a, stream) : launch_t<128, 2 / QB, QB>(a, stream);
+  return q128 ? launch_t<64, 4 / QB, QB>(a, stream) : launch_t<64, 2 / QB, QB>(a, stream);
 }
 
 }  // namespace sa
