@@ -1,22 +1,22 @@
 // mainloop.h -- the pipelined key-tile loop shared by the skip-softmax, N:M and proxy kernels.
 //
-// One workgroup of NW wavefronts, each owning QB blocks of 32 query rows, walks a sequence of 64-key tiles
-// ("steps") given by a policy object.  K and V tiles are copied HBM/L2 -> LDS with buffer loads
-// that write LDS directly (no staging registers), double-buffered.  Scores run two tiles ahead of
-// the softmax, so every tile is decided one full iteration before its V tile is needed:
+// One workgroup of NW wavefronts, each owning QB blocks of 32 query rows, walks a sequence of
+// 64-key tiles ("steps") given by a policy object.  K and V tiles are copied HBM/L2 -> LDS with
+// buffer loads that write LDS directly (no staging registers), double-buffered.  Scores run two
+// tiles ahead of the softmax and every tile's votes are published one barrier before its V tile
+// is requested, so each iteration needs a single barrier:
 //
-//   iteration j (S(j), S(j+1) computed and decided; in flight: V(j), K(j+2), V(j+1))
-//     1  wait for V(j) and K(j+2); barrier
-//     2  issue K(j+3)
-//     3  [kept(j)]   softmax(j) fused with O += P(j) V(j), 16 keys at a time (VALU || MFMA)
-//     4  S(j+2) = QK^T(j+2) into the registers S(j) used; mask; row max
-//     5  wave vote "some row of j+2 not negligible"; barrier; keep(j+2) = OR of the votes
-//     6  [kept(j+2)] issue V(j+2)
+//   iteration j (S(j) in registers and decided; S(j+1) in registers, votes written)
+//     1  wait for V(j), K(j+2); barrier (also publishes the votes of j+1)
+//     2  keep(j+1) = OR of its votes; [kept] raise mt, request V(j+1)
+//     3  request K(j+3)
+//     4  [kept(j)]  softmax(j) fused with O += P(j) V(j), 16 keys at a time (VALU || MFMA)
+//     5  S(j+2) = QK^T(j+2) into the registers S(j) used; mask; row max; wave votes for j+2
 //
 // A skipped tile costs its QK^T, row max and vote only: no exponentials, no V traffic, no P.V.
-// Loads are issued in the order ..., V(j), K(j+2), V(j+1), K(j+3), V(j+2), ...; each wait is an
-// explicit s_waitcnt vmcnt that leaves only the newest V in flight.  Cross-wave barriers are
-// "s_waitcnt lgkmcnt(0); s_barrier" (vote stores must land, prefetches must not drain).
+// Every load of iteration j-1 is complete at step 1 of iteration j (s_waitcnt vmcnt(0)).
+// Cross-wave barriers are "s_waitcnt lgkmcnt(0); s_barrier" (vote stores must land, prefetches
+// must not drain).
 //
 // Exponent reference: P = 2^(t - m_ref), m_ref raised (and O, l rescaled) only when a kept tile's
 // row max exceeds it by more than kRescaleSlack, so P <= 2^kRescaleSlack; numerator and
@@ -265,13 +265,18 @@ struct Mainloop {
     if constexpr (Pol::kFilter) pol.filter(step, s, ts.kbits, lane);
   }
 
-  // Vote through LDS; one barrier.  A kept tile raises the decision max mt at once.
-  __device__ __forceinline__ void decide(int step, TS& ts) {
+  // Each wave publishes "some row of this tile is not negligible" in LDS; the votes are read
+  // after the next barrier.
+  __device__ __forceinline__ void vote(int step, const TS& ts) {
     if constexpr (Pol::kDecide) {
       const bool wave_keep = __builtin_amdgcn_ballot_w64(!pol.negligible(ts.M, mt, lane)) != 0ull;
       if (lane == 0) sm.vote[step & 1][wave] = wave_keep ? 1 : 0;
     }
-    lds_barrier();
+  }
+
+  // After a barrier that follows every wave's vote(step): the decision.  A kept tile raises the
+  // decision max mt at once and has its V tile fetched.
+  __device__ __forceinline__ void resolve(int step, TS& ts) {
     ts.keep = true;
     if constexpr (Pol::kDecide) {
       int any = 0;
@@ -282,26 +287,27 @@ struct Mainloop {
     if (ts.keep) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) mt[qb] = fmaxf(mt[qb], ts.M[qb]);
+      issue_v(step);
     }
     pol.record(step, ts.keep, ts.M, wave, lane, tid);
   }
 
-  // iteration j: S(j) in sa (state ta), S(j+1) decided (state tb); S(j+2) is written into sa.
-  __device__ __forceinline__ void iteration(int j, f32x16 (&sa)[2][QB], TS& ta, const TS& tb) {
-    // 1: V(j) and K(j+2) landed; V(j+1), the newest load, may still be in flight
-    if (tb.keep) wait_vmcnt<kN>(); else wait_vmcnt<0>();
+  // iteration j.  On entry S(j) is in sa with keep(j) resolved (V(j) requested when kept), S(j+1)
+  // is in sb (state tb) with its votes written, K(j+2) is requested.  One barrier per iteration.
+  __device__ __forceinline__ void iteration(int j, f32x16 (&sa)[2][QB], TS& ta, TS& tb) {
+    // 1: V(j), K(j+2) and the votes of j+1 are complete and visible to every wave
+    wait_vmcnt<0>();
     lds_barrier();
-    // 2: prefetch K(j+3) into the buffer K(j+1) used
+    // 2: decide j+1 and request its V tile (the buffer V(j-1) used)
+    if (j + 1 < n) resolve(j + 1, tb);
+    // 3: request K(j+3) (the buffer K(j+1) used)
     if (j + 3 < n) issue_k(j + 3);
-    // 3: softmax(j) fused with O += P(j) V(j)
+    // 4: softmax(j) fused with O += P(j) V(j)
     if (ta.keep) softmax_pv<D, QB>(pol, j, sa, ta, mref, l, o, sm.v[j & 1], c32, lane);
-    // 4-6: S(j+2), its vote, its V tile
+    // 5: S(j+2) into sa, its row maxima and votes (mt already holds every kept tile up to j+1)
     if (j + 2 < n) {
       scores(j + 2, sa, ta);
-      decide(j + 2, ta);
-      if (ta.keep) issue_v(j + 2);
-    } else {
-      ta.keep = false;
+      vote(j + 2, ta);
     }
   }
 
@@ -316,25 +322,22 @@ struct Mainloop {
     }
     f32x16 sa[2][QB], sb[2][QB];
     TS ta, tb;
-    // prologue: K(0), K(1); S(0), keep(0), V(0); K(2); S(1), keep(1), V(1)
+    // prologue: K(0), K(1); S(0) and keep(0) (V(0) requested); S(1) and its votes; K(2)
     issue_k(0);
     if (n > 1) issue_k(1);
     if (n > 1) wait_vmcnt<kN>(); else wait_vmcnt<0>();
     lds_barrier();
     scores(0, sa, ta);
-    decide(0, ta);
-    if (ta.keep) issue_v(0);
-    tb.keep = false;
+    vote(0, ta);
+    lds_barrier();
+    resolve(0, ta);
     if (n > 1) {
-      if (n > 2) issue_k(2);   // K(0)'s buffer: every wave passed the vote barrier after QK(0)
-      // K(1) landed: in flight after it are V(0) (if kept) and K(2) (if any)
-      if (ta.keep && n > 2) wait_vmcnt<2 * kN>();
-      else if (ta.keep || n > 2) wait_vmcnt<kN>();
-      else wait_vmcnt<0>();
+      // K(1) landed: only V(0) (if kept) was requested after it
+      if (ta.keep) wait_vmcnt<kN>(); else wait_vmcnt<0>();
       lds_barrier();
       scores(1, sb, tb);
-      decide(1, tb);
-      if (tb.keep) issue_v(1);
+      vote(1, tb);
+      if (n > 2) issue_k(2);   // K(0)'s buffer: every wave passed a barrier after QK(0)
     }
     for (int j = 0; j < n; j += 2) {
       iteration(j, sa, ta, tb);

@@ -112,12 +112,17 @@ __device__ __forceinline__ void qk_tile(const char* ldsK, const bf16x8 (&qf)[QB]
   bf16x8 f[NF];
 #pragma unroll
   for (int i = 0; i < kPrefetch; ++i) f[i] = frag(i);
+  // The scheduler would otherwise sink each read next to its MFMA (fewest live registers) and
+  // expose the full LDS latency on every step; the scheduling barriers keep the reads kPrefetch
+  // steps ahead.
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NF; ++i) {
     if (i + kPrefetch < NF) f[i + kPrefetch] = frag(i + kPrefetch);
     const int kb = i / KS, ks = i % KS;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma32(f[i], qf[qb][ks], ks == 0 ? f32x16{} : s[kb][qb]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
