@@ -38,8 +38,8 @@ constexpr int kWavesPerSimd = QB == 1 ? 2 : 1;
 
 template <int D, int NW>
 struct Smem {
-  char k[2][kKeysPerTile * D * 2];
-  char v[2][kKeysPerTile * D * 2];
+  char k[2][KLayout<D>::kBytes];
+  char v[2][VLayout<D>::kBytes];
   int vote[2][NW];
 };
 
@@ -63,38 +63,22 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int D, int NW>
+template <class L, int NW>
 struct Dma {
-  static constexpr int kTileBytes = kKeysPerTile * D * 2;
-  static constexpr int kPerWave = kTileBytes / 1024 / NW;   // 1 KiB per wave-wide instruction
-  static constexpr int kRowsPerInst = 1024 / (D * 2);
-  static constexpr int kChunksPerRow = D / 8;
-  static constexpr int kPeriod = D == 128 ? 16 : 8;          // rows after which chunk_swizzle repeats
-  static constexpr int kStepRows = NW * kRowsPerInst;        // rows between a wave's instructions
-  static constexpr int kClasses = kStepRows >= kPeriod ? 1 : kPeriod / kStepRows;
-  static_assert(kPerWave >= 1 && kTileBytes % (1024 * NW) == 0, "tile must split over the waves");
-  static_assert(kPerWave % kClasses == 0 && (kClasses * kStepRows) % kPeriod == 0, "swizzle period");
+  static constexpr int kPerWave = L::kBlocks / NW;   // one block (1 KiB) per wave-wide instruction
+  static_assert(kPerWave >= 1 && L::kBlocks % NW == 0, "tile must split over the waves");
 
-  // Instruction i of wave w fills rows (w + i*NW)*kRowsPerInst + lane/kChunksPerRow.  Rows that are
-  // kClasses*kStepRows apart share their chunk permutation, so a lane's byte offset inside the
-  // tile is off[i % kClasses] plus a uniform row shift that goes into the buffer resource base.
-  // Lane l of an instruction lands at byte 1024*(w + i*NW) + 16*l, i.e. row r, physical chunk p;
-  // it fetches logical chunk p ^ f(r), so logical chunk c of row r ends at physical c ^ f(r).
+  // Lane byte offset of a block copy relative to the block's first row (the same for every block:
+  // the row shift of block b goes into the buffer resource base).
   struct LaneOffsets {
-    int off[kClasses];
+    int off;
   };
-  static __device__ __forceinline__ LaneOffsets lane_offsets(int stride_b, int wave, int lane) {
-    LaneOffsets lo;
-#pragma unroll
-    for (int c = 0; c < kClasses; ++c) {
-      const int row = wave * kRowsPerInst + c * kStepRows + lane / kChunksPerRow;
-      lo.off[c] = row * stride_b + chunk_swizzle<D>(row, lane % kChunksPerRow) * 16;
-    }
-    return lo;
+  static __device__ __forceinline__ LaneOffsets lane_offsets(int stride_b, int, int lane) {
+    return LaneOffsets{L::dma_lane(stride_b, lane)};
   }
 
   // Copy a 64-row tile whose first row starts at `base` (`bytes` valid bytes from there; rows past
-  // them arrive as zeros) into the LDS tile at `lds`.
+  // them arrive as zeros) into the LDS tile at `lds` (layout L): wave w copies blocks w, w + NW, ...
   //
   // Issued from inline asm: the compiler, seeing an LDS-writing load it cannot disambiguate,
   // would otherwise wait for every outstanding copy (vmcnt(0)) before each later LDS read and
@@ -106,13 +90,14 @@ struct Dma {
     const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
-      const int shift = (i / kClasses) * kClasses * kStepRows * stride_b;   // uniform
+      const int blk = wave + i * NW;
+      const int shift = blk * L::kRowShiftPerBlock * stride_b;   // uniform
       const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
           (void*)((const char*)base + shift), (short)0, max(0, bytes - shift), 0x00020000);
-      const unsigned dst = lds0 + (wave + i * NW) * 1024;
+      const unsigned dst = lds0 + blk * L::kPitch;
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                    :
-                   : "s"(dst), "v"(lo.off[i % kClasses]), "s"(rsrc)
+                   : "s"(dst), "v"(lo.off), "s"(rsrc)
                    : "memory", "m0");
     }
   }
@@ -172,19 +157,16 @@ __device__ __forceinline__ void softmax_pv(const Pol& pol, int step, const f32x1
   bool weighted = false;
   if constexpr (Pol::kWeighted) weighted = pol.weighted(step);
 
-  const int g = lane >> 4, j = lane & 15, h = lane >> 5;
   // V^T operands of chunk n (16 keys: kb = n/2, c = n%2) for each 32-wide d block: two transpose
   // reads each, issued one chunk ahead of the MFMAs that consume them.
   auto vt = [&](int n, bf16x8 (&a)[D / 32]) {
     const int kb = n >> 1, c = n & 1;
-    const int row = kb * 32 + c * 16 + 4 * h + (j >> 2);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const int col = db * 32 + 16 * (g & 1) + 4 * (j & 3);
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(ldsV + tile_offset<D>(row, col)));
+          (lds_i16x4*)(ldsV + VLayout<D>::v_off(lane, kb, c, 0, db)));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(ldsV + tile_offset<D>(row + 8, col)));
+          (lds_i16x4*)(ldsV + VLayout<D>::v_off(lane, kb, c, 1, db)));
       a[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
@@ -231,13 +213,16 @@ __device__ __forceinline__ void softmax_pv(const Pol& pol, int step, const f32x1
 // partials of this lane (l still to be summed over the two lane halves).
 template <int D, int NW, int QB, class Pol>
 struct Mainloop {
-  using DmaT = Dma<D, NW>;
+  using DmaK = Dma<KLayout<D>, NW>;
+  using DmaV = Dma<VLayout<D>, NW>;
   using TS = TileState<QB>;
-  static constexpr int kN = DmaT::kPerWave;   // loads per tile per lane
+  static constexpr int kN = DmaK::kPerWave;   // loads per tile per lane
+  static_assert(DmaK::kPerWave == DmaV::kPerWave, "K and V tiles take the same number of copies");
 
   Pol& pol;
   Smem<D, NW>& sm;
-  typename DmaT::LaneOffsets klo, vlo;
+  typename DmaK::LaneOffsets klo;
+  typename DmaV::LaneOffsets vlo;
   const bf16x8 (&qf)[QB][D / 16];
   f32x16 (&o)[D / 32][QB];
   float (&mref)[QB];
@@ -248,11 +233,11 @@ struct Mainloop {
 
   __device__ __forceinline__ void issue_k(int step) {
     const TileSrc t = pol.src(step);
-    DmaT::copy(sm.k[step & 1], t.k, t.k_bytes, t.k_stride_b, klo, wave);
+    DmaK::copy(sm.k[step & 1], t.k, t.k_bytes, t.k_stride_b, klo, wave);
   }
   __device__ __forceinline__ void issue_v(int step) {
     const TileSrc t = pol.src(step);
-    DmaT::copy(sm.v[step & 1], t.v, t.v_bytes, t.v_stride_b, vlo, wave);
+    DmaV::copy(sm.v[step & 1], t.v, t.v_bytes, t.v_stride_b, vlo, wave);
   }
 
   // S(step) from the K tile in LDS, masked, with its row maxima and N:M bits.
@@ -317,8 +302,8 @@ struct Mainloop {
     if (n <= 0) return;
     {
       const TileSrc t = pol.src(0);
-      klo = DmaT::lane_offsets(t.k_stride_b, wave, lane);
-      vlo = DmaT::lane_offsets(t.v_stride_b, wave, lane);
+      klo = DmaK::lane_offsets(t.k_stride_b, wave, lane);
+      vlo = DmaV::lane_offsets(t.v_stride_b, wave, lane);
     }
     f32x16 sa[2][QB], sb[2][QB];
     TS ta, tb;

@@ -172,13 +172,14 @@ void proxy_kernel(ProxyArgs a) {
     const __bf16* kmean = (const __bf16*)a.k_mean + sbase;
     const __bf16* vsum = (const __bf16*)a.v_sum + sbase;
     const int n_tiles = (nKB + kKeysPerTile - 1) / kKeysPerTile;
-    const auto slo = Dma<D, NW>::lane_offsets(D * 2, wave, lane);
+    const auto sklo = Dma<KLayout<D>, NW>::lane_offsets(D * 2, wave, lane);
+    const auto svlo = Dma<VLayout<D>, NW>::lane_offsets(D * 2, wave, lane);
     for (int t = 0; t < n_tiles; ++t) {
       const int r0 = t * kKeysPerTile;
       const int bytes = (nKB - r0) * D * 2;
       lds_barrier();   // every wave is done with the buffers the loop above (or tile t-1) used
-      Dma<D, NW>::copy(sm.k[0], kmean + (int64_t)r0 * D, bytes, D * 2, slo, wave);
-      Dma<D, NW>::copy(sm.v[0], vsum + (int64_t)r0 * D, bytes, D * 2, slo, wave);
+      Dma<KLayout<D>, NW>::copy(sm.k[0], kmean + (int64_t)r0 * D, bytes, D * 2, sklo, wave);
+      Dma<VLayout<D>, NW>::copy(sm.v[0], vsum + (int64_t)r0 * D, bytes, D * 2, svlo, wave);
       wait_vmcnt<0>();
       lds_barrier();
       f32x16 s[2][QB];

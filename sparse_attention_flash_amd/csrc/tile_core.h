@@ -40,22 +40,83 @@ constexpr float kLog2e = 1.4426950408889634f;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // ------------------------------------------------------------------------------------------------
-// LDS tile of 64 rows x D bf16, row pitch D*2 bytes, 16-byte chunks permuted per row.  The
-// permutation makes (a) 16 consecutive rows at one chunk index (the K reads of QK^T) hit 16
-// different chunks, and (b) the 4 aligned rows x 2 neighbouring chunks read by one transpose-read
-// group land on 8 different chunks.
+// LDS layouts of a 64-key x D bf16 tile.  A tile is a run of blocks; a direct-to-LDS copy writes
+// one 1 KiB block per wave-wide instruction (lane l -> bytes 16l..16l+15 of the block) and each
+// lane may fetch any 16-byte chunk, so placement inside and between blocks is free.  The copies
+// keep 16 consecutive lanes on 16 consecutive chunks of one key row (coalesced 256-byte rows).
+//
+// head_dim 128: block b (b < 16) holds rows b, b+16, b+32, b+48 row-major (chunk q of row
+// b + 16*rho at 16-byte slot 16*rho + q); blocks sit kPitch bytes apart.  A lane's LDS reads
+// are then base(lane) + a compile-time offset (immediate offsets, no per-step address registers),
+// and both read patterns are conflict-free through the block pitch alone:
+//   K (ds_read_b128, 16 rows at one chunk per quarter wave): rows 0..15 are in blocks 0..15 and
+//     a pitch of 65 slots puts them on 16 different 16-byte bank groups;
+//   V (ds_read_b64_tr_b16, 4 rows x 4 chunks per half wave): 4 consecutive rows are in 4
+//     consecutive blocks and a pitch of 68 slots moves each by 4 bank groups.
+//
+// head_dim 64 (one layout for K and V): 8 blocks of 8 rows x 8 chunks, row-major, chunk q of row r
+// stored at q ^ f(r) (f a bijection on 8 rows) so 8 consecutive rows at one chunk hit 8 chunks.
 // ------------------------------------------------------------------------------------------------
-template <int D>
-__device__ __forceinline__ int chunk_swizzle(int row, int chunk) {
-  int f = ((row & 3) << 1) | ((row >> 2) & 1);
-  if constexpr (D == 128) f |= ((row >> 3) & 1) << 3;
-  return chunk ^ f;
-}
+template <int D, bool kV>
+struct TileLayout;
+
+template <bool kV>
+struct TileLayout<128, kV> {
+  static constexpr int kPitch = kV ? 1088 : 1040;   // bytes per block
+  static constexpr int kBlocks = 16;
+  static constexpr int kBytes = kBlocks * kPitch;
+  // A copy of block b: lane l fetches row b + 16*(l/16), chunk l%16; the row shift b goes into
+  // the buffer resource base.
+  static constexpr int kRowShiftPerBlock = 1;
+  static __device__ __forceinline__ int dma_lane(int stride_b, int lane) {
+    return (lane >> 4) * 16 * stride_b + (lane & 15) * 16;
+  }
+  // byte offset of chunk q of row r
+  static __device__ __forceinline__ int chunk_off(int r, int q) {
+    return (r & 15) * kPitch + ((r >> 4) * 16 + q) * 16;
+  }
+  // K rows as MFMA A operands: row 32kb + lane%32, chunk 2ks + lane/32
+  static __device__ __forceinline__ int k_off(int lane, int kb, int ks) {
+    return chunk_off((lane & 31) + 32 * kb, 2 * ks + (lane >> 5));
+  }
+  // transpose-read source of lane (g = lane/16, j = lane%16): row 32kb + 16c + 4(lane/32) + j/4
+  // + 8hi, columns 32db + 16(g%2) + 4(j%4) .. +3
+  static __device__ __forceinline__ int v_off(int lane, int kb, int c, int hi, int db) {
+    const int g = lane >> 4, j = lane & 15, h = lane >> 5;
+    const int r = kb * 32 + c * 16 + 4 * h + (j >> 2) + 8 * hi;
+    return chunk_off(r, db * 4 + 2 * (g & 1) + ((j & 3) >> 1)) + (j & 1) * 8;
+  }
+};
+
+template <bool kV>
+struct TileLayout<64, kV> {
+  static constexpr int kPitch = 1024;
+  static constexpr int kBlocks = 8;
+  static constexpr int kBytes = kBlocks * kPitch;
+  static constexpr int kRowShiftPerBlock = 8;   // block b holds rows 8b..8b+7
+  static __device__ __forceinline__ int swz(int row, int chunk) {
+    return chunk ^ (((row & 3) << 1) | ((row >> 2) & 1));
+  }
+  static __device__ __forceinline__ int elem(int row, int col) {   // byte offset of (row, col)
+    return row * 128 + swz(row, col >> 3) * 16 + (col & 7) * 2;
+  }
+  static __device__ __forceinline__ int dma_lane(int stride_b, int lane) {
+    return (lane >> 3) * stride_b + swz(lane >> 3, lane & 7) * 16;
+  }
+  static __device__ __forceinline__ int k_off(int lane, int kb, int ks) {
+    const int row = kb * 32 + (lane & 31);
+    return row * 128 + swz(row, 2 * ks + (lane >> 5)) * 16;
+  }
+  static __device__ __forceinline__ int v_off(int lane, int kb, int c, int hi, int db) {
+    const int g = lane >> 4, j = lane & 15, h = lane >> 5;
+    return elem(kb * 32 + c * 16 + 4 * h + (j >> 2) + 8 * hi, db * 32 + 16 * (g & 1) + 4 * (j & 3));
+  }
+};
 
 template <int D>
-__device__ __forceinline__ int tile_offset(int row, int col) {   // byte offset of element (row, col)
-  return row * (D * 2) + chunk_swizzle<D>(row, col >> 3) * 16 + (col & 7) * 2;
-}
+using KLayout = TileLayout<D, false>;
+template <int D>
+using VLayout = TileLayout<D, true>;
 
 // Buffer resource over one (batch, head) slab of a [rows, D] bf16 tensor with the given row stride
 // (elements).  num_records covers exactly the valid rows, so buffer loads beyond the last row
@@ -103,11 +164,8 @@ __device__ __forceinline__ void qk_tile(const char* ldsK, const bf16x8 (&qf)[QB]
   constexpr int KS = D / 16;        // 16-wide k steps per 32-key block
   constexpr int NF = 2 * KS;        // fragments per tile
   constexpr int kPrefetch = 4;
-  const int h = lane >> 5, r32 = lane & 31;
   auto frag = [&](int i) {
-    const int kb = i / KS, ks = i % KS, row = kb * 32 + r32;
-    return *reinterpret_cast<const bf16x8*>(ldsK + row * (D * 2) +
-                                            chunk_swizzle<D>(row, 2 * ks + h) * 16);
+    return *reinterpret_cast<const bf16x8*>(ldsK + KLayout<D>::k_off(lane, i / KS, i % KS));
   };
   bf16x8 f[NF];
 #pragma unroll
