@@ -170,12 +170,9 @@ __device__ __forceinline__ void softmax_pv(const Pol& pol, int step, const f32x1
       a[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
-  bf16x8 va[2][D / 32];
-  vt(0, va[0]);
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
+  // P of chunk n into pb (bf16 operands) and its row sums into l
+  auto make_p = [&](int n, bf16x8 (&pb)[QB]) {
     const int kb = n >> 1, c = n & 1;
-    bf16x8 pb[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float rs = 0.f;
@@ -193,11 +190,33 @@ __device__ __forceinline__ void softmax_pv(const Pol& pol, int step, const f32x1
       }
       l[qb] += rs;
     }
-    if (n + 1 < 4) vt(n + 1, va[(n + 1) & 1]);
+  };
+  // Chunk n's MFMAs run while the exponentials of chunk n+1 are computed: the scheduling groups
+  // alternate one MFMA with a share of that VALU work.
+  constexpr int kMfma = (D / 32) * QB;
+  constexpr int kValu = (28 * QB + kMfma - 1) / kMfma;
+  bf16x8 va[2][D / 32];
+  bf16x8 pb[2][QB];
+  vt(0, va[0]);
+  make_p(0, pb[0]);
+  vt(1, va[1]);
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma32(va[n & 1][db], pb[qb], o[db][qb]);
+      for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma32(va[n & 1][db], pb[n & 1][qb], o[db][qb]);
+    if (n + 1 < 4) {
+      make_p(n + 1, pb[(n + 1) & 1]);
+#pragma unroll
+      for (int i = 0; i < kMfma; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (n + 2 < 4) vt(n + 2, va[n & 1]);
   }
 }
 
