@@ -315,10 +315,43 @@ struct Mainloop {
     }
   }
 
+  // Without decisions (N:M, exact routes) every V tile is fetched, so the scores need only one
+  // step of lookahead and a single S tile:
+  //   iteration j: wait for V(j), K(j+1); barrier; request V(j+1), K(j+2);
+  //                softmax(j) + O += P(j) V(j); S(j+1) = QK^T(j+1) into the same registers.
+  __device__ __forceinline__ void run_dense() {
+    f32x16 s[2][QB];
+    TS ts;
+    issue_k(0);
+    issue_v(0);
+    if (n > 1) issue_k(1);
+    if (n > 1) wait_vmcnt<2 * kN>(); else wait_vmcnt<kN>();   // K(0) landed
+    lds_barrier();
+    scores(0, s, ts);
+    for (int j = 0; j < n; ++j) {
+      wait_vmcnt<0>();   // V(j), K(j+1)
+      lds_barrier();
+      if (j + 1 < n) issue_v(j + 1);   // the buffer V(j-1) used
+      if (j + 2 < n) issue_k(j + 2);   // the buffer K(j) used
+      pol.record(j, true, ts.M, wave, lane, tid == 0);
+      softmax_pv<D, QB>(pol, j, s, ts, mref, l, o, sm.v[j & 1], c32, lane);
+      if (j + 1 < n) scores(j + 1, s, ts);
+    }
+  }
+
   __device__ __forceinline__ void run() {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mt[qb] = -INFINITY;
     if (n <= 0) return;
+    if constexpr (!Pol::kDecide) {
+      {
+        const TileSrc t = pol.src(0);
+        klo = DmaK::lane_offsets(t.k_stride_b, wave, lane);
+        vlo = DmaV::lane_offsets(t.v_stride_b, wave, lane);
+      }
+      run_dense();
+      return;
+    }
     {
       const TileSrc t = pol.src(0);
       klo = DmaK::lane_offsets(t.k_stride_b, wave, lane);

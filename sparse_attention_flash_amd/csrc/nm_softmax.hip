@@ -55,6 +55,18 @@ __device__ __forceinline__ void group_ranks(const float (&own)[4], const float (
   }
 }
 
+// This lane's 32 keys of a 64-key tile, bit b = kb*16 + r, sit at key offsets
+// p(b) = kb*32 + (r/4)*8 + 4h + r%4, which increase with b: the keys with offset < T are the
+// low bits, as many as there are such offsets.
+__device__ __forceinline__ uint32_t bits_below(int T, int h) {
+  int cnt = 0;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cnt += min(max(T - (kb * 32 + q * 8 + 4 * h), 0), 4);
+  return cnt >= 32 ? 0xFFFFFFFFu : ((1u << cnt) - 1u);
+}
+
 template <int D, int NW, int QB, int M>
 struct NmPolicy {
   static constexpr bool kDecide = false, kFilter = true, kWeighted = false;
@@ -89,9 +101,9 @@ struct NmPolicy {
     }
   }
 
-  // keep bit (kb*16 + r) of bits[qb]: key not masked and (dense, or top-n of its group).  All
-  // per-element tests are sign-bit arithmetic; the sink/recent windows and masked keys only occur
-  // on a few tiles per row, tested once per tile.
+  // keep bit (kb*16 + r) of bits[qb]: key not masked and (dense, or top-n of its group).  The
+  // ranks are sign-bit arithmetic per element; the sink/recent windows and masked keys are key
+  // ranges, turned into bit ranges (bits_below) on the few tiles per row that touch them.
   __device__ __forceinline__ void filter(int j, const f32x16 (&s)[2][QB], uint32_t (&bits)[QB],
                                          int lane) const {
     const int k0 = j * kKeysPerTile;
@@ -118,30 +130,17 @@ struct NmPolicy {
 #pragma unroll
           for (int e = 0; e < 4; ++e)   // top-n: rank - n < 0
             kb_bits |= ((uint32_t)(rank[e] - n) >> 31) << (kb * 16 + 4 * gi + e);
+          // one group at a time: the scheduler would otherwise interleave all eight groups'
+          // comparisons and run out of registers
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (any_dense) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + (r >> 2) * 8 + 4 * h + (r & 3);
-            const int d = row - key;   // dense: key < sink, or 0 <= d < recent
-            const uint32_t dense = ((uint32_t)(key - sink) >> 31) |
-                                   ((~(uint32_t)d >> 31) & ((uint32_t)(d - recent) >> 31));
-            kb_bits |= dense << (kb * 16 + r);
-          }
+      if (any_dense) {   // key < sink, or row - recent < key <= row
+        kb_bits |= bits_below(sink - k0, h);
+        if (recent > 0) kb_bits |= bits_below(row - k0 + 1, h) & ~bits_below(row - recent - k0 + 1, h);
       }
-      if (any_masked) {   // masked keys hold -inf
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const uint32_t x = __float_as_uint(s[kb][qb][r]) ^ 0xFF800000u;   // 0 iff -inf
-            const uint32_t live = (x | (0u - x)) >> 31;
-            kb_bits &= ~((live ^ 1u) << (kb * 16 + r));
-          }
-      }
+      if (any_masked)    // key < Sk and (causal) key <= row
+        kb_bits &= bits_below(causal ? min(Sk, row + 1) - k0 : Sk - k0, h);
       bits[qb] = kb_bits;
       if (keep_bits != nullptr || scores != nullptr) export_row(k0, row, qb, kb_bits, s, lane);
     }
@@ -154,19 +153,23 @@ struct NmPolicy {
     const int64_t rbase = row_base + row;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      uint32_t word = 0u;   // this lane's 16 bits of the 32-key word, merged with lane^32's
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        word |= ((kb_bits >> (kb * 16 + r)) & 1u) << ((r >> 2) * 8 + 4 * h + (r & 3));
+      // this lane's 16 bits sit at key offsets (r/4)*8 + 4h + r%4: spread the nibbles 8 apart,
+      // then shift by 4h; merged with lane^32's half
+      const uint32_t x = (kb_bits >> (kb * 16)) & 0xFFFFu;
+      uint32_t word = ((x & 0xFu) | ((x & 0xF0u) << 4) | ((x & 0xF00u) << 8) |
+                       ((x & 0xF000u) << 12)) << (4 * h);
       word |= __float_as_uint(other_half(__uint_as_float(word), lane));
       if (row < Sq) {
         if (keep_bits != nullptr && h == 0 && k0 + kb * 32 < Sk)
           keep_bits[rbase * W + k0 / 32 + kb] = word;
         if (scores != nullptr) {
+          int kbase = k0 + 4 * h;   // key = kbase + c, c a compile-time constant
+          asm volatile("" : "+v"(kbase));
+          float* dst = scores + rbase * Sk + kbase;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = k0 + tile_key(kb, r, lane);
-            if (key < Sk) scores[rbase * Sk + key] = s[kb][qb][r];
+            const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+            if (kbase + c < Sk) dst[c] = s[kb][qb][r];
           }
         }
       }
@@ -176,7 +179,7 @@ struct NmPolicy {
   __device__ __forceinline__ bool negligible(const float (&)[QB], const float (&)[QB], int) const {
     return false;
   }
-  __device__ __forceinline__ void record(int, bool, const float (&)[QB], int, int, int) {}
+  __device__ __forceinline__ void record(int, bool, const float (&)[QB], int, int, bool) {}
 };
 
 template <int D, int NW, int QB, int M>
