@@ -11,6 +11,7 @@ Each wrapper returns results in natural layouts:
   (0 kept, 1 skipped, 2 not visited), ``rowmax [B,Hq,nQT,nKT,Br]`` (log2 domain, float64).
 * ``nm_softmax``: ``o``, ``lse``, ``keep_bits [B,Hq,Sq,ceil(Sk/32)]`` (uint32, LSB first).
 * ``route_prep``: ``n_exact``, ``exact_idx`` (ascending, -1 padded), ``proxy_keep``.
+* ``bsr_route_prep``: the same triple from BSR rows, plus the count of non-canonical rows.
 * ``proxy_fwd``: ``o``, ``lse``.
 * ``threshold``: ``(scale_factor, lambda, log2_lambda)`` as Python floats.
 
@@ -60,6 +61,8 @@ def _load():
         lib.oracle_nm_softmax.restype = I
         lib.oracle_route_prep.argtypes = [I64, I, P, P, P, P]
         lib.oracle_route_prep.restype = I
+        lib.oracle_bsr_route_prep.argtypes = [I64, I, P, I64, P, P, P, P, P]
+        lib.oracle_bsr_route_prep.restype = I
         lib.oracle_proxy_fwd.argtypes = [I] * 8 + [D, P, P, P, P, P, P, I, P, I64, P, P]
         lib.oracle_proxy_fwd.restype = I
         lib.oracle_threshold.argtypes = [D, D, D, I64, P, P, P]
@@ -165,6 +168,24 @@ def route_prep(bitmask, n_kv_blocks):
     if rc:
         raise ValueError("oracle_route_prep rejected its arguments")
     return (n_exact.reshape(lead), idx.reshape(*lead, n_kv_blocks), keep.reshape(*lead, W))
+
+
+def bsr_route_prep(indptr, indices, n_kv_blocks):
+    """Route stream from BSR rows (indptr of rows+1 entries, indices); returns the route_prep
+    triple plus the number of non-canonical rows."""
+    ip = np.ascontiguousarray(indptr, dtype=np.int32).ravel()
+    ix = np.ascontiguousarray(indices, dtype=np.int32).ravel()
+    rows = ip.size - 1
+    W = -(-n_kv_blocks // 32)
+    n_exact = np.zeros(rows, np.int32)
+    idx = np.zeros((rows, n_kv_blocks), np.int32)
+    keep = np.zeros((rows, W), np.uint32)
+    bad = np.zeros(1, np.int64)
+    rc = _load().oracle_bsr_route_prep(rows, n_kv_blocks, _ptr(ip), ix.size, _ptr(ix),
+                                       _ptr(n_exact), _ptr(idx), _ptr(keep), _ptr(bad))
+    if rc:
+        raise ValueError("oracle_bsr_route_prep rejected its arguments")
+    return n_exact, idx, keep, int(bad[0])
 
 
 def proxy_fwd(q, k, v, k_mean, v_sum, bitmask, *, block_q, block_k, scale, use_proxy,

@@ -328,6 +328,57 @@ int oracle_route_prep(int64_t rows, int nKB, const uint32_t* bitmask, int32_t* n
 }
 
 /* ------------------------------------------------------------------------------------------------
+ * Route preparation from canonical BSR (block_indptr / block_indices).  [FI-proxy] "Bitmask format":
+ * BSR and bitmap inputs are prepared into the same route stream, and the two give bitwise-identical
+ * results.  Integer and exact, written as its definition:
+ *
+ *   row r (one per (b, kv head, q block), row-major) lists the exact blocks
+ *       E_r = { indices[e] : indptr[r] <= e < indptr[r+1], 0 <= indices[e] < nKB }
+ *   outputs as for the bitmap: n_exact = |E_r|, E_r ascending then -1, proxy_keep = blocks j < nKB
+ *   not in E_r.
+ *
+ * Readings: a row is a set of block indices, so duplicates collapse and entry order does not
+ * matter; entries outside [0, nKB) are dropped; a row whose pointer range is reversed or leaves
+ * [0, nnz] is clamped to [0, nnz] (empty when reversed).  *bad_rows counts the rows that are not
+ * canonical: a pointer out of range or reversed, an entry outside [0, nnz) or [0, nKB), or entries
+ * that are not strictly ascending.
+ * ----------------------------------------------------------------------------------------------*/
+int oracle_bsr_route_prep(int64_t rows, int nKB, const int32_t* indptr, int64_t nnz,
+                          const int32_t* indices, int32_t* n_exact, int32_t* exact_idx,
+                          uint32_t* proxy_keep, int64_t* bad_rows) {
+    if (rows < 0 || nKB < 1 || nnz < 0) return 1;
+    const int W = (nKB + 31) / 32;
+    unsigned char* in_set = (unsigned char*)malloc((size_t)nKB);
+    if (in_set == NULL) return 2;
+    int64_t bad = 0;
+    for (int64_t row = 0; row < rows; ++row) {
+        const int64_t p0 = indptr[row], p1 = indptr[row + 1];
+        int is_bad = p0 < 0 || p1 < p0 || p1 > nnz;
+        int64_t start = p0 < 0 ? 0 : (p0 > nnz ? nnz : p0);
+        int64_t end = p1 < start ? start : (p1 > nnz ? nnz : p1);
+        memset(in_set, 0, (size_t)nKB);
+        for (int64_t e = start; e < end; ++e) {
+            const int32_t j = indices[e];
+            if (j < 0 || j >= nKB) is_bad = 1;
+            else in_set[j] = 1;
+            if (e > start && indices[e - 1] >= j) is_bad = 1;
+        }
+        int count = 0;
+        for (int w = 0; w < W; ++w) proxy_keep[row * W + w] = 0u;
+        for (int j = 0; j < nKB; ++j) {
+            if (in_set[j]) exact_idx[row * nKB + count++] = j;
+            else proxy_keep[row * W + (j >> 5)] |= 1u << (j & 31);
+        }
+        for (int j = count; j < nKB; ++j) exact_idx[row * nKB + j] = -1;
+        n_exact[row] = count;
+        bad += is_bad;
+    }
+    free(in_set);
+    *bad_rows = bad;
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------------
  * Proxy-compensated block-sparse forward.  [FI-proxy] "Description" and "Bitmask format".  A
  * closed-form approximation, written as its definition:
  *

@@ -58,6 +58,58 @@ def test_route_prep_padding_ignored_and_all_ones():
     assert (n_exact == nKB).all() and (idx == np.arange(nKB)).all() and (keep == 0).all()
 
 
+@pytest.mark.parametrize("nKB", [1, 31, 33, 128, 255])
+def test_bsr_route_matches_bitmask_route(nKB):
+    # "Bitmask format": BSR and bitmap inputs prepare into the same route stream and give
+    # bitwise-identical results.
+    bm = W.gen_bitmask(44, 2, 3, 5, nKB, max(1, nKB // 4), garbage_padding=True)
+    indptr, indices = W.bitmask_to_bsr(bm, nKB)
+    ref = oracle.route_prep(bm, nKB)
+    n_exact, idx, keep, bad = oracle.bsr_route_prep(indptr, indices, nKB)
+    assert bad == 0
+    for x, y in zip(ref, (n_exact, idx, keep)):
+        assert np.array_equal(x.reshape(y.shape), y)
+
+
+def test_bsr_route_worked_example():
+    # Three rows over nKB = 40 blocks (W = 2 words, 8 valid bits in the second):
+    #   row 0: {0, 5, 39}, canonical;  row 1: empty;  row 2: [33, 2, 2, 40, -1] -> {2, 33}, not
+    #   canonical (unsorted, duplicate, two entries out of range).
+    indptr = np.array([0, 3, 3, 8], np.int32)
+    indices = np.array([0, 5, 39, 33, 2, 2, 40, -1], np.int32)
+    n_exact, idx, keep, bad = oracle.bsr_route_prep(indptr, indices, 40)
+    assert n_exact.tolist() == [3, 0, 2]
+    assert idx[0, :4].tolist() == [0, 5, 39, -1] and (idx[1] == -1).all()
+    assert idx[2, :3].tolist() == [2, 33, -1] and (idx[:, 3:] == -1).all()
+    assert keep.tolist() == [[0xFFFFFFDE, 0x7F], [0xFFFFFFFF, 0xFF], [0xFFFFFFFB, 0xFD]]
+    assert bad == 1
+
+
+def test_bsr_route_rows_are_sets():
+    # Shuffling a row, repeating an entry or adding out-of-range entries leaves its route unchanged;
+    # exactly those rows are reported as non-canonical.
+    nKB = 70
+    bm = W.gen_bitmask(45, 1, 4, 9, nKB, 20)
+    indptr, indices = W.bitmask_to_bsr(bm, nKB)
+    ref = oracle.bsr_route_prep(indptr, indices, nKB)
+    ip2, ix2, scrambled = W.scramble_bsr(46, indptr, indices, nKB)
+    got = oracle.bsr_route_prep(ip2, ix2, nKB)
+    assert scrambled.any() and not scrambled.all()
+    assert got[3] == int(scrambled.sum())
+    for x, y in zip(ref[:3], got[:3]):
+        assert np.array_equal(x, y)
+
+
+def test_bsr_route_bad_pointers_are_clamped():
+    # A reversed pointer pair is an empty row; a range past nnz is cut at nnz.  Both are counted.
+    indptr = np.array([0, 2, 1, 4], np.int32)
+    indices = np.array([1, 3, 5], np.int32)
+    n_exact, idx, keep, bad = oracle.bsr_route_prep(indptr, indices, 8)
+    assert n_exact.tolist() == [2, 0, 2]
+    assert idx[0, :2].tolist() == [1, 3] and idx[2, :2].tolist() == [3, 5]
+    assert bad == 2
+
+
 def _proxy(q, k, v, bm, Bq, Bk, use_proxy, km=None, vs=None):
     if km is None:
         km, vs = W.block_summaries(k, v, Bk)

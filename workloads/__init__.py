@@ -179,6 +179,39 @@ def gen_bitmask(seed, B, Hkv, n_q_blocks, n_kv_blocks, n_set, garbage_padding=Fa
     return out
 
 
+def bitmask_to_bsr(bitmask, n_kv_blocks):
+    """Canonical BSR of a packed bitmap: (indptr [rows+1] int32, indices [nnz] int32), rows in the
+    bitmap's (b, kv head, q block) order, each row's valid set blocks in ascending order."""
+    bm = np.ascontiguousarray(bitmask, dtype=np.uint32)
+    by = bm.view(np.uint8).reshape(-1, bm.shape[-1] * 4)
+    bits = np.unpackbits(by, axis=-1, bitorder="little")[:, :n_kv_blocks].astype(bool)
+    counts = bits.sum(-1)
+    indptr = np.zeros(bits.shape[0] + 1, np.int32)
+    indptr[1:] = np.cumsum(counts)
+    indices = np.nonzero(bits)[1].astype(np.int32)   # row-major: rows in order, columns ascending
+    return indptr, indices
+
+
+def scramble_bsr(seed, indptr, indices, n_kv_blocks, frac=0.5):
+    """Non-canonical copy of a BSR: in about ``frac`` of the rows the entries are shuffled and
+    receive a duplicate and an out-of-range entry.  Returns (indptr, indices, scrambled_rows)."""
+    rng = _rng(seed, 31)
+    rows = indptr.size - 1
+    new_ptr = [0]
+    new_idx = []
+    scrambled = np.zeros(rows, bool)
+    for r in range(rows):
+        ent = list(indices[indptr[r]:indptr[r + 1]])
+        if ent and rng.random() < frac:
+            ent.append(ent[int(rng.integers(len(ent)))])
+            ent.append(int(rng.choice([-1, n_kv_blocks, n_kv_blocks + 7])))
+            ent = list(rng.permutation(ent))
+            scrambled[r] = True
+        new_idx += ent
+        new_ptr.append(len(new_idx))
+    return np.array(new_ptr, np.int32), np.array(new_idx, np.int32), scrambled
+
+
 def block_summaries(k_bits, v_bits, block_k):
     """Per-KV-block mean of K and sum of V over the block's true tokens: bf16 [B,Hkv,nKB,D]."""
     kf = bf16_bits_to_f32(k_bits).astype(np.float64)
