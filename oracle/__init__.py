@@ -14,6 +14,7 @@ Each wrapper returns results in natural layouts:
 * ``bsr_route_prep``: the same triple from BSR rows, plus the count of non-canonical rows.
 * ``proxy_fwd``: ``o``, ``lse``.
 * ``threshold``: ``(scale_factor, lambda, log2_lambda)`` as Python floats.
+* ``fit_threshold``: ``(a, b, s_min, s_max)`` of the log-space calibration fit.
 
 When ``units`` (linear (b, hq, query-tile) indices) is given, only those units are computed and
 the results come back per unit: ``o [n, Br, D]``, ``lse [n, Br]``, ``tile_state [n, nKT]`` ...
@@ -67,6 +68,8 @@ def _load():
         lib.oracle_proxy_fwd.restype = I
         lib.oracle_threshold.argtypes = [D, D, D, I64, P, P, P]
         lib.oracle_threshold.restype = I
+        lib.oracle_fit_threshold.argtypes = [I, P, P, I64, P, P, P, P]
+        lib.oracle_fit_threshold.restype = I
         _lib = lib
     return _lib
 
@@ -222,3 +225,15 @@ def threshold(a, b, target_sparsity, seq_k):
     if rc:
         raise ValueError("oracle_threshold rejected its arguments")
     return sf.value, lam.value, l2.value
+
+
+def fit_threshold(lambdas, sparsities, seq_k):
+    lam = np.ascontiguousarray(lambdas, dtype=np.float64)
+    sp = np.ascontiguousarray(sparsities, dtype=np.float64)
+    assert lam.shape == sp.shape
+    out = [ctypes.c_double() for _ in range(4)]
+    rc = _load().oracle_fit_threshold(lam.size, _ptr(lam), _ptr(sp), int(seq_k),
+                                      *[ctypes.addressof(o) for o in out])
+    if rc:
+        raise ValueError("oracle_fit_threshold: fewer than two usable trials")
+    return tuple(o.value for o in out)

@@ -490,3 +490,47 @@ int oracle_threshold(double a, double b, double target_sparsity, int64_t seq_k,
     *log2_lambda = log2(*lambda);
     return 0;
 }
+
+/* ------------------------------------------------------------------------------------------------
+ * Log-space calibration fit.  [MO-diff] introduction ("Calibrated threshold": scale_factor =
+ * a*exp(b*target_sparsity) calibrated once, log-space fitting recommended) and "Known Issues"
+ * (targets below the smallest sparsity reached extrapolate); [MO-llm] "Custom Configuration"
+ * (threshold_trials).  Each trial i ran the kernel at threshold lambda_i and measured tile sparsity
+ * s_i; its scale factor is lambda_i * seq_k.  The fit is ordinary least squares of
+ *     y_i = ln(lambda_i * seq_k)  on  x_i = s_i:   b = sum (x-xm)(y-ym) / sum (x-xm)^2,
+ *                                                 ln a = ym - b*xm,
+ * over the usable trials (lambda_i > 0 finite, 0 < s_i < 1; a trial with no skipped tile or with
+ * every tile skipped says nothing about where the curve is).  Also returns the smallest and the
+ * largest usable sparsity.  Fails (returns 1) with fewer than two usable trials or when all usable
+ * sparsities are equal.
+ * ----------------------------------------------------------------------------------------------*/
+int oracle_fit_threshold(int n, const double* lambdas, const double* sparsities, int64_t seq_k,
+                         double* a_out, double* b_out, double* s_min, double* s_max) {
+    if (n < 0 || seq_k < 1) return 1;
+    int used = 0;
+    double xm = 0.0, ym = 0.0, lo = INFINITY, hi = -INFINITY;
+    for (int i = 0; i < n; ++i) {
+        const double lam = lambdas[i], s = sparsities[i];
+        if (!(lam > 0.0) || !isfinite(lam) || !(s > 0.0 && s < 1.0)) continue;
+        xm += s;
+        ym += log(lam * (double)seq_k);
+        lo = s < lo ? s : lo;
+        hi = s > hi ? s : hi;
+        ++used;
+    }
+    if (used < 2 || !(hi > lo)) return 1;
+    xm /= used;
+    ym /= used;
+    double sxy = 0.0, sxx = 0.0;
+    for (int i = 0; i < n; ++i) {
+        const double lam = lambdas[i], s = sparsities[i];
+        if (!(lam > 0.0) || !isfinite(lam) || !(s > 0.0 && s < 1.0)) continue;
+        sxy += (s - xm) * (log(lam * (double)seq_k) - ym);
+        sxx += (s - xm) * (s - xm);
+    }
+    *b_out = sxy / sxx;
+    *a_out = exp(ym - *b_out * xm);
+    *s_min = lo;
+    *s_max = hi;
+    return 0;
+}
