@@ -265,6 +265,26 @@ def run_paths(torch, sa, W, to_dev, steps, warmup):
 
 
 # ------------------------------------------------------------------------------------------------
+def calibration(sa, W, qd, kd, vd, o, cnt, wl, S):
+    """Calibration sweep over the pages' trial thresholds on the headline workload, the log-space
+    fit of the measured sparsities, and the sparsity reached when targets are lowered through the
+    fitted model (untimed)."""
+    trials = W.THRESHOLD_TRIALS
+    kw = dict(causal=wl.causal, block_q=wl.block_q, block_k=wl.block_k)
+    t0 = time.perf_counter()
+    sp = sa.sa_skip_softmax_calibrate(qd, kd, vd, o, trials, cnt, **kw)
+    a, b, lo, hi = sa.sa_fit_threshold_calib(trials, sp, S)
+    reached = {}
+    for target in (0.5, 0.7):
+        _, lam, _ = sa.sa_threshold_from_calib(a, b, target, S)
+        reached[str(target)] = {"lambda": lam, "sparsity": round(
+            sa.sa_skip_softmax_calibrate(qd, kd, vd, o, [lam], cnt, **kw)[0], 4)}
+    cnt.zero_()
+    return {"trials": trials, "sparsity": [round(x, 4) for x in sp], "fit_a": a, "fit_b": b,
+            "fit_range": [lo, hi], "targets": reached,
+            "sweep_and_fit_s": round(time.perf_counter() - t0, 3)}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -359,6 +379,7 @@ def main():
                   "between steps",
     }
     if not args.no_paths:
+        result["calibration"] = calibration(sa, W, qd, kd, vd, o, cnt, wl, S)
         del qd, kd, vd, o
         torch.cuda.empty_cache()
         result["paths"] = run_paths(torch, sa, W, to_dev, args.steps, args.warmup)

@@ -130,6 +130,30 @@ sa_status sa_bitmask_route_prep(const sa_attn_desc* desc, const uint32_t* bitmas
                                 void* stream);
 
 /*
+ * Route preparation from canonical BSR, the other "plan" input (FlashInfer proxy description,
+ * "Bitmask format": BSR block_indptr / block_indices and bitmaps are prepared into the same route
+ * stream, with bitwise-identical results).  Rows r = (b, kv head, q block), row-major, nQB, nKB as
+ * for sa_bitmask_route_prep.
+ *
+ *   block_indptr   int32 [B*Hkv*nQB + 1]: row r owns entries block_indptr[r] .. block_indptr[r+1]-1.
+ *   block_indices  int32 [nnz]: exact KV block indices (may be NULL when nnz == 0).  A canonical
+ *                  row is strictly ascending within [0, nKB).
+ *   nnz            length of block_indices; no entry at or past it is read.
+ *   n_exact, exact_idx, proxy_keep   exactly as sa_bitmask_route_prep produces them for the bitmap
+ *                  holding the same blocks.
+ *   bad_rows       optional uint32 [1], caller-zeroed: incremented once per row that is not
+ *                  canonical (pointer outside [0, nnz] or reversed, entry outside [0, nKB),
+ *                  entries not strictly ascending).
+ * Non-canonical rows are still prepared as sets: duplicates collapse, order is ignored, entries
+ * outside [0, nKB) are dropped, and a pointer range is clamped to [0, nnz] (empty when reversed).
+ * Requires nKB <= 65536 (SA_ERR_UNSUPPORTED otherwise).  Only the shape fields of desc are used.
+ */
+sa_status sa_bsr_route_prep(const sa_attn_desc* desc, const int32_t* block_indptr,
+                            const int32_t* block_indices, int64_t nnz, int32_t* n_exact,
+                            int32_t* exact_idx, uint32_t* proxy_keep, uint32_t* bad_rows,
+                            void* stream);
+
+/*
  * Proxy-compensated block-sparse forward, the "run" step (FlashInfer proxy description,
  * "Description").  For a query in block qb: exact blocks from (n_exact, exact_idx) contribute
  * their tokens exactly; when use_proxy != 0, every block j with bit j set in proxy_keep contributes
@@ -158,6 +182,38 @@ sa_status sa_proxy_block_sparse_fwd(const sa_attn_desc* desc, const void* q, con
 sa_status sa_threshold_from_calib(double a, double b, double target_sparsity, int64_t seq_k,
                                   double* scale_factor_out, float* lambda_out,
                                   float* log2_lambda_out);
+
+/*
+ * Calibration sweep (Model-Optimizer diffusion README, "Calibrated threshold"; HuggingFace
+ * attention-sparsity page, calibration.threshold_trials): runs sa_skip_softmax_fwd once per trial
+ * threshold on the same inputs and returns each trial's tile sparsity, skipped / visited tiles
+ * summed over all (batch, query head) counters.
+ *
+ *   o               bf16 output, overwritten by every trial (a work buffer for the caller).
+ *   trial_lambdas   host float [n_trials], each >= 0 and finite (SA_ERR_VALUE otherwise).
+ *   head_counters   device uint32 [B, Hq, 2] work buffer; the call zeroes it before each trial.
+ *   sparsities_out  host double [n_trials].
+ * Unlike the other entry points this one blocks: after each trial it copies the counters to the
+ * host and synchronizes the stream.  Shape rules as sa_skip_softmax_fwd.
+ */
+sa_status sa_skip_softmax_calibrate(const sa_attn_desc* desc, const void* q, const void* k,
+                                    const void* v, void* o, const float* trial_lambdas,
+                                    int32_t n_trials, uint32_t* head_counters,
+                                    double* sparsities_out, void* stream);
+
+/*
+ * Log-space fit of the calibrated threshold model, host only (Model-Optimizer diffusion README:
+ * scale_factor = a*exp(b*target_sparsity) calibrated once, log-space fitting recommended;
+ * "Known Issues": targets below the smallest sparsity reached extrapolate).  Each trial i ran at
+ * threshold lambda_i with measured tile sparsity s_i, i.e. scale factor lambda_i * seq_k.  Ordinary
+ * least squares of ln(lambda_i * seq_k) on s_i over the usable trials (lambda_i > 0 finite and
+ * 0 < s_i < 1) gives b (slope) and ln a (intercept).  min/max_sparsity_out (optional) receive the
+ * range of usable sparsities: targets outside it are extrapolations.  SA_ERR_VALUE when fewer than
+ * two usable trials remain or their sparsities are all equal.
+ */
+sa_status sa_fit_threshold_calib(const double* trial_lambdas, const double* sparsities,
+                                 int32_t n_trials, int64_t seq_k, double* a_out, double* b_out,
+                                 double* min_sparsity_out, double* max_sparsity_out);
 
 #ifdef __cplusplus
 }

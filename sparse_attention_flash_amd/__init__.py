@@ -4,7 +4,7 @@ The functions here carry the C ABI's names (``include/sa.h``) and only marshal a
 shapes and strides become an ``sa_attn_desc``, tensors become device pointers, and the current
 torch stream becomes the ``hipStream_t``.  Every step of the computation runs in the HIP kernels of
 ``libsa_hip.so``; there is no fallback path.  Importing this package fails if the library has not
-been built (``python -m sparse_attention_flash_amd.build``).
+been built (``python sparse_attention_flash_amd/build.py``).
 
 Tensors: Q/O ``[B, Sq, Hq, D]`` and K/V ``[B, Sk, Hkv, D]`` bf16 on the GPU with a unit stride on
 D; optional outputs are preallocated by the caller with the shapes given in ``sa.h``.
@@ -21,7 +21,7 @@ _DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_DIR, "libsa_hip.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_attention_flash_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python sparse_attention_flash_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -54,10 +54,16 @@ _lib.sa_nm_softmax_fwd.argtypes = [_DESC, _P, _P, _P, _P, _I32, _I32, _I32, _I32
 _lib.sa_nm_softmax_fwd.restype = ctypes.c_int
 _lib.sa_bitmask_route_prep.argtypes = [_DESC, _P, _P, _P, _P, _P]
 _lib.sa_bitmask_route_prep.restype = ctypes.c_int
+_lib.sa_bsr_route_prep.argtypes = [_DESC, _P, _P, ctypes.c_int64, _P, _P, _P, _P, _P]
+_lib.sa_bsr_route_prep.restype = ctypes.c_int
 _lib.sa_proxy_block_sparse_fwd.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P]
 _lib.sa_proxy_block_sparse_fwd.restype = ctypes.c_int
 _lib.sa_threshold_from_calib.argtypes = [_D, _D, _D, ctypes.c_int64, _P, _P, _P]
 _lib.sa_threshold_from_calib.restype = ctypes.c_int
+_lib.sa_skip_softmax_calibrate.argtypes = [_DESC, _P, _P, _P, _P, _P, _I32, _P, _P, _P]
+_lib.sa_skip_softmax_calibrate.restype = ctypes.c_int
+_lib.sa_fit_threshold_calib.argtypes = [_P, _P, _I32, ctypes.c_int64, _P, _P, _P, _P]
+_lib.sa_fit_threshold_calib.restype = ctypes.c_int
 
 raw = _lib   # the ctypes handle, for callers that pass raw pointers
 
@@ -156,6 +162,22 @@ def sa_bitmask_route_prep(bitmask, n_exact, exact_idx, proxy_keep, *, batch, hea
            "sa_bitmask_route_prep")
 
 
+def sa_bsr_route_prep(block_indptr, block_indices, n_exact, exact_idx, proxy_keep, *, batch,
+                      heads_kv, seqlen_q, seqlen_k, block_q, block_k, bad_rows=None, stream=None):
+    d = sa_attn_desc()
+    d.batch, d.heads_kv, d.heads_q = batch, heads_kv, heads_kv
+    d.seqlen_q, d.seqlen_k, d.block_q, d.block_k = seqlen_q, seqlen_k, block_q, block_k
+    for t in (block_indptr, block_indices, n_exact, exact_idx, proxy_keep, bad_rows):
+        if t is not None and (t.dtype not in (torch.int32, torch.uint32) or not t.is_contiguous()):
+            raise TypeError("route tensors must be contiguous 32-bit integer tensors")
+    nnz = block_indices.numel()
+    _check(_lib.sa_bsr_route_prep(ctypes.byref(d), _ptr(block_indptr),
+                                  _ptr(block_indices) if nnz else None, nnz, _ptr(n_exact),
+                                  _ptr(exact_idx), _ptr(proxy_keep), _ptr(bad_rows),
+                                  _stream(stream)),
+           "sa_bsr_route_prep")
+
+
 def sa_proxy_block_sparse_fwd(q, k, v, k_mean, v_sum, n_exact, exact_idx, proxy_keep, use_proxy,
                               o, *, block_q=128, block_k=128, scale=None, lse=None, stream=None):
     d = make_desc(q, k, v, o, causal=False, block_q=block_q, block_k=block_k, scale=scale)
@@ -177,6 +199,34 @@ def sa_threshold_from_calib(a, b, target_sparsity, seq_k):
                                         ctypes.addressof(l2)),
            "sa_threshold_from_calib")
     return sf.value, lam.value, l2.value
+
+
+def sa_skip_softmax_calibrate(q, k, v, o, trial_lambdas, head_counters, *, causal=False,
+                              block_q=128, block_k=64, scale=None, stream=None):
+    """Tile sparsity of each trial threshold (a list of floats); blocks until done."""
+    d = make_desc(q, k, v, o, causal=causal, block_q=block_q, block_k=block_k, scale=scale)
+    trials = (ctypes.c_float * len(trial_lambdas))(*map(float, trial_lambdas))
+    out = (ctypes.c_double * len(trial_lambdas))()
+    _check(_lib.sa_skip_softmax_calibrate(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                          ctypes.addressof(trials), len(trial_lambdas),
+                                          _ptr(head_counters), ctypes.addressof(out),
+                                          _stream(stream)),
+           "sa_skip_softmax_calibrate")
+    return list(out)
+
+
+def sa_fit_threshold_calib(trial_lambdas, sparsities, seq_k):
+    """(a, b, min_sparsity, max_sparsity) of the log-space fit."""
+    n = len(trial_lambdas)
+    if len(sparsities) != n:
+        raise ValueError("one sparsity per trial")
+    lam = (ctypes.c_double * n)(*map(float, trial_lambdas))
+    sp = (ctypes.c_double * n)(*map(float, sparsities))
+    out = [ctypes.c_double() for _ in range(4)]
+    _check(_lib.sa_fit_threshold_calib(ctypes.addressof(lam), ctypes.addressof(sp), n, int(seq_k),
+                                       *[ctypes.addressof(o) for o in out]),
+           "sa_fit_threshold_calib")
+    return tuple(o.value for o in out)
 
 
 def tile_counts(seqlen_q, seqlen_k, block_q, block_k):

@@ -1,6 +1,6 @@
 """Build libsa_hip.so (the gfx950 kernels and the C ABI) in-tree with hipcc.
 
-    python -m sparse_attention_flash_amd.build
+    python sparse_attention_flash_amd/build.py
 
 Every ``csrc/*.hip`` file is compiled for gfx950 only and linked into one shared library next to
 this file.  Packed-fp32 instruction selection is disabled for all device code.

@@ -6,6 +6,7 @@
 // not passed to the kernels) and enqueued on the caller's stream.
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "kernels.h"
 #include "sa.h"
@@ -162,6 +163,34 @@ sa_status sa_bitmask_route_prep(const sa_attn_desc* desc, const uint32_t* bitmas
   return from_hip(sa::launch_route_prep(a, (hipStream_t)stream));
 }
 
+sa_status sa_bsr_route_prep(const sa_attn_desc* desc, const int32_t* block_indptr,
+                            const int32_t* block_indices, int64_t nnz, int32_t* n_exact,
+                            int32_t* exact_idx, uint32_t* proxy_keep, uint32_t* bad_rows,
+                            void* stream) {
+  if (desc == nullptr || block_indptr == nullptr || n_exact == nullptr || exact_idx == nullptr ||
+      proxy_keep == nullptr || (nnz > 0 && block_indices == nullptr))
+    return SA_ERR_NULL;
+  if (desc->batch < 1 || desc->heads_kv < 1 || desc->seqlen_q < 1 || desc->seqlen_k < 1 ||
+      desc->block_q < 1 || desc->block_k < 1 || nnz < 0)
+    return SA_ERR_SHAPE;
+  sa::BsrRouteArgs a{};
+  const int64_t nQB = ((int64_t)desc->seqlen_q + desc->block_q - 1) / desc->block_q;
+  const int64_t nKB = ((int64_t)desc->seqlen_k + desc->block_k - 1) / desc->block_k;
+  if (nKB > 32 * (int64_t)sa::kBsrMaxWords) return SA_ERR_UNSUPPORTED;
+  a.nKB = (int)nKB;
+  a.W = (a.nKB + 31) / 32;
+  a.rows = (int64_t)desc->batch * desc->heads_kv * nQB;
+  if (a.rows > INT32_MAX) return SA_ERR_SHAPE;
+  a.indptr = block_indptr;
+  a.indices = block_indices;
+  a.nnz = nnz;
+  a.n_exact = n_exact;
+  a.exact_idx = exact_idx;
+  a.proxy_keep = proxy_keep;
+  a.bad_rows = bad_rows;
+  return from_hip(sa::launch_bsr_route_prep(a, (hipStream_t)stream));
+}
+
 sa_status sa_proxy_block_sparse_fwd(const sa_attn_desc* desc, const void* q, const void* k,
                                     const void* v, const void* k_mean, const void* v_sum,
                                     const int32_t* n_exact, const int32_t* exact_idx,
@@ -199,6 +228,80 @@ sa_status sa_threshold_from_calib(double a, double b, double target_sparsity, in
   if (scale_factor_out != nullptr) *scale_factor_out = sf;
   if (lambda_out != nullptr) *lambda_out = lam32;
   if (log2_lambda_out != nullptr) *log2_lambda_out = (float)std::log2((double)lam32);
+  return SA_OK;
+}
+
+sa_status sa_skip_softmax_calibrate(const sa_attn_desc* desc, const void* q, const void* k,
+                                    const void* v, void* o, const float* trial_lambdas,
+                                    int32_t n_trials, uint32_t* head_counters,
+                                    double* sparsities_out, void* stream) {
+  if (trial_lambdas == nullptr || sparsities_out == nullptr || head_counters == nullptr)
+    return SA_ERR_NULL;
+  if (n_trials < 1) return SA_ERR_VALUE;
+  for (int32_t i = 0; i < n_trials; ++i)
+    if (!(trial_lambdas[i] >= 0.f) || !std::isfinite(trial_lambdas[i])) return SA_ERR_VALUE;
+  sa_status st = check_attention(desc, q, k, v, o);
+  if (st != SA_OK) return st;
+  if (desc->block_k != 64) return SA_ERR_UNSUPPORTED;
+  const hipStream_t s = (hipStream_t)stream;
+  const size_t n_heads = (size_t)desc->batch * desc->heads_q;
+  std::vector<uint32_t> host(2 * n_heads);
+  for (int32_t i = 0; i < n_trials; ++i) {
+    if (hipMemsetAsync(head_counters, 0, host.size() * sizeof(uint32_t), s) != hipSuccess)
+      return SA_ERR_HIP;
+    st = sa_skip_softmax_fwd(desc, q, k, v, o, trial_lambdas[i], nullptr, head_counters, nullptr,
+                             nullptr, stream);
+    if (st != SA_OK) return st;
+    if (hipMemcpyAsync(host.data(), head_counters, host.size() * sizeof(uint32_t),
+                       hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return SA_ERR_HIP;
+    uint64_t visited = 0, skipped = 0;
+    for (size_t h = 0; h < n_heads; ++h) {
+      visited += host[2 * h];
+      skipped += host[2 * h + 1];
+    }
+    sparsities_out[i] = visited ? (double)skipped / (double)visited : 0.0;
+  }
+  return SA_OK;
+}
+
+sa_status sa_fit_threshold_calib(const double* trial_lambdas, const double* sparsities,
+                                 int32_t n_trials, int64_t seq_k, double* a_out, double* b_out,
+                                 double* min_sparsity_out, double* max_sparsity_out) {
+  if (trial_lambdas == nullptr || sparsities == nullptr || a_out == nullptr || b_out == nullptr)
+    return SA_ERR_NULL;
+  if (n_trials < 0 || seq_k < 1) return SA_ERR_VALUE;
+  // a trial tells where the curve lies only when some but not all tiles were skipped
+  auto usable = [&](int32_t i) {
+    return trial_lambdas[i] > 0.0 && std::isfinite(trial_lambdas[i]) && sparsities[i] > 0.0 &&
+           sparsities[i] < 1.0;
+  };
+  int used = 0;
+  double sx = 0.0, sy = 0.0, lo = INFINITY, hi = -INFINITY;
+  for (int32_t i = 0; i < n_trials; ++i) {
+    if (!usable(i)) continue;
+    ++used;
+    sx += sparsities[i];
+    sy += std::log(trial_lambdas[i] * (double)seq_k);
+    lo = std::fmin(lo, sparsities[i]);
+    hi = std::fmax(hi, sparsities[i]);
+  }
+  if (used < 2 || !(hi > lo)) return SA_ERR_VALUE;
+  const double mx = sx / used, my = sy / used;
+  double cov = 0.0, var = 0.0;
+  for (int32_t i = 0; i < n_trials; ++i) {
+    if (!usable(i)) continue;
+    const double dx = sparsities[i] - mx;
+    cov += dx * (std::log(trial_lambdas[i] * (double)seq_k) - my);
+    var += dx * dx;
+  }
+  const double b = cov / var, a = std::exp(my - b * mx);
+  if (!std::isfinite(a) || !std::isfinite(b) || !(a > 0.0)) return SA_ERR_VALUE;
+  *a_out = a;
+  *b_out = b;
+  if (min_sparsity_out != nullptr) *min_sparsity_out = lo;
+  if (max_sparsity_out != nullptr) *max_sparsity_out = hi;
   return SA_OK;
 }
 

@@ -44,6 +44,21 @@ struct RouteArgs {
   int nKB, W;
 };
 
+// BSR rows are expanded into an LDS bitmap of at most this many words (nKB <= 32 * kBsrMaxWords).
+constexpr int kBsrMaxWords = 2048;
+
+struct BsrRouteArgs {
+  const int32_t* indptr;                // [rows + 1]
+  const int32_t* indices;               // [nnz]
+  int64_t nnz;
+  int32_t* n_exact;
+  int32_t* exact_idx;
+  uint32_t* proxy_keep;
+  uint32_t* bad_rows;                   // optional
+  int64_t rows;                         // B * Hkv * nQB
+  int nKB, W;
+};
+
 struct ProxyArgs {
   AttnGeom g;
   const void* k_mean;
@@ -58,6 +73,7 @@ struct ProxyArgs {
 hipError_t launch_skip_softmax(const SkipArgs& a, hipStream_t stream);
 hipError_t launch_nm_softmax(const NmArgs& a, hipStream_t stream);
 hipError_t launch_route_prep(const RouteArgs& a, hipStream_t stream);
+hipError_t launch_bsr_route_prep(const BsrRouteArgs& a, hipStream_t stream);
 hipError_t launch_proxy(const ProxyArgs& a, hipStream_t stream);
 
 }  // namespace sa

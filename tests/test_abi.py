@@ -26,7 +26,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol():
     names = declared_entry_points()
-    assert {"sa_skip_softmax_fwd", "sa_nm_softmax_fwd", "sa_bitmask_route_prep",
+    assert {"sa_skip_softmax_fwd", "sa_nm_softmax_fwd", "sa_bitmask_route_prep", "sa_bsr_route_prep",
             "sa_proxy_block_sparse_fwd", "sa_threshold_from_calib", "sa_status_str"} <= set(names)
     lib = ctypes.CDLL(sa.LIB_PATH)
     for n in names:
@@ -106,6 +106,20 @@ def test_route_prep_rejects():
     assert sa.raw.sa_bitmask_route_prep(ctypes.byref(d0), FAKE, FAKE, FAKE, FAKE, None) == sa.SA_ERR_SHAPE
 
 
+def test_bsr_route_prep_rejects():
+    d = _desc(block_k=128)
+    f = sa.raw.sa_bsr_route_prep
+    assert f(ctypes.byref(d), None, FAKE, 4, FAKE, FAKE, FAKE, None, None) == sa.SA_ERR_NULL
+    assert f(ctypes.byref(d), FAKE, None, 4, FAKE, FAKE, FAKE, None, None) == sa.SA_ERR_NULL
+    assert f(None, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None, None) == sa.SA_ERR_NULL
+    assert f(ctypes.byref(d), FAKE, FAKE, -1, FAKE, FAKE, FAKE, None, None) == sa.SA_ERR_SHAPE
+    d0 = _desc(block_k=0)
+    assert f(ctypes.byref(d0), FAKE, FAKE, 4, FAKE, FAKE, FAKE, None, None) == sa.SA_ERR_SHAPE
+    big = _desc(block_k=1)
+    big.seqlen_k = 32 * 2048 + 1
+    assert f(ctypes.byref(big), FAKE, FAKE, 4, FAKE, FAKE, FAKE, None, None) == sa.SA_ERR_UNSUPPORTED
+
+
 def _proxy(d, use_proxy=1, km=FAKE, vs=FAKE, routes=FAKE):
     return sa.raw.sa_proxy_block_sparse_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, km, vs, routes,
                                             FAKE, FAKE, use_proxy, FAKE, None, None)
@@ -132,3 +146,39 @@ def test_threshold_matches_oracle_and_rejects():
         with pytest.raises(sa.SaError) as e:
             sa.sa_threshold_from_calib(*args)
         assert e.value.status == sa.SA_ERR_VALUE
+
+
+def test_fit_threshold_matches_oracle_and_rejects():
+    import numpy as np
+    rng = np.random.default_rng(11)
+    s = np.concatenate([np.sort(rng.uniform(0.25, 0.85, 10)), [0.0, 1.0]])
+    lam = 1443.49 * np.exp(4.30 * s + rng.normal(0, 0.2, s.size)) / 32760
+    got = sa.sa_fit_threshold_calib(lam, s, 32760)
+    ref = oracle.fit_threshold(lam, s, 32760)
+    for g, r in zip(got, ref):
+        assert g == pytest.approx(r, rel=1e-12)
+    for lams, sps in [([0.1, 0.2], [0.5, 0.5]), ([0.1, 0.2], [0.0, 0.4]), ([0.0, 0.2], [0.3, 0.4])]:
+        with pytest.raises(sa.SaError) as e:
+            sa.sa_fit_threshold_calib(lams, sps, 100)
+        assert e.value.status == sa.SA_ERR_VALUE
+    assert sa.raw.sa_fit_threshold_calib(None, FAKE, 2, 10, FAKE, FAKE, None, None) == sa.SA_ERR_NULL
+
+
+def test_calibrate_rejects():
+    d = _desc()
+    f = sa.raw.sa_skip_softmax_calibrate
+
+    def call(trials, n=None, counters=FAKE, out=True, desc=d):
+        arr = (ctypes.c_float * max(1, len(trials)))(*trials)
+        res = (ctypes.c_double * max(1, len(trials)))()
+        return f(ctypes.byref(desc) if desc is not None else None, FAKE, FAKE, FAKE, FAKE,
+                 ctypes.addressof(arr), len(trials) if n is None else n, counters,
+                 ctypes.addressof(res) if out else None, None)
+
+    assert call([0.1], counters=None) == sa.SA_ERR_NULL
+    assert call([0.1], out=False) == sa.SA_ERR_NULL
+    assert call([0.1], n=0) == sa.SA_ERR_VALUE
+    assert call([0.1, -1.0]) == sa.SA_ERR_VALUE
+    assert call([float("nan")]) == sa.SA_ERR_VALUE
+    assert call([0.1], desc=None) == sa.SA_ERR_NULL
+    assert call([0.1], desc=_desc(block_k=128)) == sa.SA_ERR_UNSUPPORTED

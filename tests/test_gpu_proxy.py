@@ -1,5 +1,6 @@
-"""GPU parity of sa_bitmask_route_prep (bit-exact) and sa_proxy_block_sparse_fwd (max-abs 2e-2,
-mean-abs 2e-3 against the float64 oracle), needs an MI355X."""
+"""GPU parity of sa_bitmask_route_prep and sa_bsr_route_prep (bit-exact) and
+sa_proxy_block_sparse_fwd (max-abs 2e-2, mean-abs 2e-3 against the float64 oracle), needs an
+MI355X."""
 import math
 
 import numpy as np
@@ -46,6 +47,53 @@ def test_route_prep_bit_exact(S, Bk):
     assert np.array_equal(ne.cpu().numpy(), r_ne)
     assert np.array_equal(ix.cpu().numpy(), r_ix)
     assert np.array_equal(kp.cpu().numpy().view(np.uint32), r_kp)
+
+
+def bsr_route_gpu(indptr, indices, B, Hkv, Sq, Sk, Bq, Bk):
+    nQB, nKB = -(-Sq // Bq), -(-Sk // Bk)
+    Wd = -(-nKB // 32)
+    n_exact = torch.full((B, Hkv, nQB), -7, dtype=torch.int32, device="cuda")
+    idx = torch.full((B, Hkv, nQB, nKB), -7, dtype=torch.int32, device="cuda")
+    keep = torch.full((B, Hkv, nQB, Wd), -7, dtype=torch.int32, device="cuda")
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sa.sa_bsr_route_prep(i32(indptr), i32(indices), n_exact, idx, keep, batch=B, heads_kv=Hkv,
+                         seqlen_q=Sq, seqlen_k=Sk, block_q=Bq, block_k=Bk, bad_rows=bad)
+    return n_exact, idx, keep, bad
+
+
+@pytest.mark.parametrize("S,Bk", [(64, 64), (257, 64), (16257, 128), (32760, 64), (300000, 64)])
+def test_bsr_route_prep_matches_bitmask(S, Bk):
+    # "Bitmask format": BSR and bitmap routes are bitwise identical.
+    announce(f"bsr route prep S={S} Bk={Bk}")
+    B, Hkv, Bq = 2, 3, 128
+    nQB, nKB = min(-(-S // Bq), 40), -(-S // Bk)
+    Sq = nQB * Bq
+    bm = W.gen_bitmask(53, B, Hkv, nQB, nKB, max(1, nKB // 4), garbage_padding=True)
+    indptr, indices = W.bitmask_to_bsr(bm, nKB)
+    got = bsr_route_gpu(indptr, indices, B, Hkv, Sq, S, Bq, Bk)
+    ref = route_gpu(bm, B, Hkv, Sq, S, Bq, Bk)
+    torch.cuda.synchronize()
+    for x, y in zip(got[:3], ref):
+        assert torch.equal(x, y)
+    assert int(got[3].item()) == 0
+
+
+def test_bsr_route_prep_non_canonical_rows():
+    announce("bsr route prep, non-canonical rows")
+    B, Hkv, Bq, Bk, S = 1, 4, 128, 64, 4500
+    nQB, nKB = -(-S // Bq), -(-S // Bk)
+    bm = W.gen_bitmask(54, B, Hkv, nQB, nKB, 20)
+    indptr, indices = W.bitmask_to_bsr(bm, nKB)
+    ip2, ix2, scrambled = W.scramble_bsr(55, indptr, indices, nKB)
+    ip2[5], ip2[6] = ip2[6], ip2[5]          # one reversed pointer pair (rows 4 and 5 change)
+    ip2[-1] = ix2.size + 3                   # last row runs past nnz: clamped
+    ne, ix, kp, bad = bsr_route_gpu(ip2, ix2, B, Hkv, S, S, Bq, Bk)
+    torch.cuda.synchronize()
+    r_ne, r_ix, r_kp, r_bad = oracle.bsr_route_prep(ip2, ix2, nKB)
+    assert np.array_equal(ne.cpu().numpy().ravel(), r_ne)
+    assert np.array_equal(ix.cpu().numpy().reshape(r_ix.shape), r_ix)
+    assert np.array_equal(kp.cpu().numpy().view(np.uint32).reshape(r_kp.shape), r_kp)
+    assert int(bad.item()) == r_bad and r_bad >= int(scrambled.sum())
 
 
 def run_proxy(q, k, v, bm, Bq, Bk, use_proxy):

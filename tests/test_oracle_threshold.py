@@ -111,3 +111,10 @@ def test_fit_ignores_trials_without_information():
         oracle.fit_threshold(lam2[3:], s2[3:], seq_k)
     with pytest.raises(ValueError):
         oracle.fit_threshold([0.1, 0.2], [0.5, 0.5], seq_k)
+
+
+def test_workload_constants_are_the_pages():
+    import workloads as W
+    c = _consts()
+    assert (W.CALIB_A, W.CALIB_B) == (c["calibration_prefill"]["a"], c["calibration_prefill"]["b"])
+    assert W.THRESHOLD_TRIALS == c["threshold_trials"]["values"]

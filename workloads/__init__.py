@@ -232,6 +232,8 @@ def block_summaries(k_bits, v_bits, block_k):
 # ---------------------------------------------------------------------------------------------
 CALIB_A = 1443.49   # prefill coefficients of the calibrated threshold model (Wan 2.2 example)
 CALIB_B = 4.30
+# calibration.threshold_trials of the HuggingFace attention-sparsity page's custom configuration
+THRESHOLD_TRIALS = [1e-4, 5e-4, 1e-3, 5e-3, 1e-2, 2e-2, 5e-2, 1e-1, 2e-1, 3e-1, 5e-1, 7e-1]
 
 
 @dataclasses.dataclass(frozen=True)
