@@ -10,6 +10,8 @@ Each wrapper returns results in natural layouts:
 * ``skip_softmax``: ``o [B,Sq,Hq,D]`` (float64), ``lse [B,Hq,Sq]``, ``tile_state [B,Hq,nQT,nKT]``
   (0 kept, 1 skipped, 2 not visited), ``rowmax [B,Hq,nQT,nKT,Br]`` (log2 domain, float64).
 * ``nm_softmax``: ``o``, ``lse``, ``keep_bits [B,Hq,Sq,ceil(Sk/32)]`` (uint32, LSB first).
+* ``skip_nm_softmax``: ``o``, ``lse``, ``tile_state``, ``rowmax`` as skip_softmax, plus
+  ``keep_bits`` as nm_softmax.
 * ``route_prep``: ``n_exact``, ``exact_idx`` (ascending, -1 padded), ``proxy_keep``.
 * ``bsr_route_prep``: the same triple from BSR rows, plus the count of non-canonical rows.
 * ``proxy_fwd``: ``o``, ``lse``.
@@ -60,6 +62,9 @@ def _load():
         lib.oracle_skip_softmax.restype = I
         lib.oracle_nm_softmax.argtypes = [I] * 8 + [D, I, I, I, I, P, P, P, I, P, P, P, I64, P, P, P]
         lib.oracle_nm_softmax.restype = I
+        lib.oracle_skip_nm_softmax.argtypes = ([I] * 9 + [D, D] + [I] * 4 + [P, P, P, I] +
+                                               [P] * 5 + [I64] + [P] * 5)
+        lib.oracle_skip_nm_softmax.restype = I
         lib.oracle_route_prep.argtypes = [I64, I, P, P, P, P]
         lib.oracle_route_prep.restype = I
         lib.oracle_bsr_route_prep.argtypes = [I64, I, P, I64, P, P, P, P, P]
@@ -155,6 +160,44 @@ def nm_softmax(q, k, v, *, causal, scale, n, m, sink, recent, block_q=64, mode=0
     lse = lse.reshape(B, Hq, nQT * block_q)[:, :, :Sq]
     kb = kb.reshape(B, Hq, nQT * block_q, W)[:, :, :Sq]
     return np.ascontiguousarray(o), np.ascontiguousarray(lse), np.ascontiguousarray(kb)
+
+
+def skip_nm_softmax(q, k, v, *, causal, block_q, block_k, scale, lam, n, m, sink, recent, mode=0,
+                    rowmax_in=None, state_in=None, scores_in=None, keep_in=None, units=None):
+    q, k, v = _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v")
+    B, Sq, Hq, D = q.shape
+    _, Sk, Hkv, _ = k.shape
+    nQT, nKT, W = -(-Sq // block_q), -(-Sk // block_k), -(-Sk // 32)
+    u, cnt = _units(units, B * Hq * nQT)
+    if mode == 1:
+        rowmax_in = np.ascontiguousarray(rowmax_in, dtype=np.float32)
+        assert rowmax_in.size == B * Hq * nQT * nKT * block_q
+        scores_in = np.ascontiguousarray(scores_in, dtype=np.float32)
+        assert scores_in.size == B * Hq * Sq * Sk
+    if mode == 2:
+        state_in = np.ascontiguousarray(state_in, dtype=np.uint8)
+        assert state_in.size == B * Hq * nQT * nKT
+        keep_in = np.ascontiguousarray(keep_in, dtype=np.uint32)
+        assert keep_in.size == B * Hq * Sq * W
+    o = np.zeros((cnt, block_q, D))
+    lse = np.zeros((cnt, block_q))
+    st = np.zeros((cnt, nKT), np.uint8)
+    rm = np.zeros((cnt, nKT, block_q))
+    kb = np.zeros((cnt, block_q, W), np.uint32)
+    rc = _load().oracle_skip_nm_softmax(
+        B, Hq, Hkv, Sq, Sk, D, int(causal), block_q, block_k, float(scale), float(lam), int(n),
+        int(m), int(sink), int(recent), _ptr(q), _ptr(k), _ptr(v), int(mode), _ptr(rowmax_in),
+        _ptr(state_in), _ptr(scores_in), _ptr(keep_in), _ptr(u), cnt, _ptr(o), _ptr(lse), _ptr(st),
+        _ptr(rm), _ptr(kb))
+    if rc:
+        raise ValueError("oracle_skip_nm_softmax rejected its arguments")
+    if units is not None:
+        return o, lse, st, rm, kb
+    o = o.reshape(B, Hq, nQT * block_q, D)[:, :, :Sq].transpose(0, 2, 1, 3)
+    lse = lse.reshape(B, Hq, nQT * block_q)[:, :, :Sq]
+    kb = kb.reshape(B, Hq, nQT * block_q, W)[:, :, :Sq]
+    return (np.ascontiguousarray(o), np.ascontiguousarray(lse), st.reshape(B, Hq, nQT, nKT),
+            rm.reshape(B, Hq, nQT, nKT, block_q), np.ascontiguousarray(kb))
 
 
 def route_prep(bitmask, n_kv_blocks):

@@ -195,6 +195,23 @@ int oracle_skip_softmax(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causa
     return bad;
 }
 
+/* N:M keep flags of one query row r over all Sk keys (the definition below, under oracle_nm_softmax):
+ * x[kk] holds the ranking scores (-inf where not allowed); keep[kk] receives allowed and (dense or
+ * rank < N). */
+static void nm_keep_row(int r, int Sk, int causal, int N, int Mg, int sink, int recent,
+                        const double* x, unsigned char* keep) {
+    for (int kk = 0; kk < Sk; ++kk) {
+        const int allowed = !causal || kk <= r;
+        const int dense = allowed && (kk < sink || (r - kk >= 0 && r - kk < recent));
+        const int g0 = (kk / Mg) * Mg;
+        const int g1 = (g0 + Mg < Sk) ? g0 + Mg : Sk;
+        int rank = 0;
+        for (int k2 = g0; k2 < g1; ++k2)
+            if (x[k2] > x[kk] || (x[k2] == x[kk] && k2 < kk)) ++rank;
+        keep[kk] = (unsigned char)(allowed && (dense || rank < N));
+    }
+}
+
 /* ------------------------------------------------------------------------------------------------
  * N:M sparse softmax forward.  [MO-llm] method list and "N:M Sparse Softmax".  The result is its
  * own definition, so this is the definition written out:
@@ -256,19 +273,11 @@ int oracle_nm_softmax(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
                 else if (mode == 1) x[kk] = (double)scores_in[row * Sk + kk];
                 else x[kk] = dot_qk(q, k, Sq, Sk, Hq, Hkv, D, b, r, hq, kk, hk);
             }
-            for (int kk = 0; kk < Sk; ++kk) {
-                const int allowed = !causal || kk <= r;
-                if (mode == 2) {
+            if (mode == 2) {
+                for (int kk = 0; kk < Sk; ++kk)
                     keep[kk] = (unsigned char)((keep_in[row * W + (kk >> 5)] >> (kk & 31)) & 1u);
-                    continue;
-                }
-                const int dense = allowed && (kk < sink || (r - kk >= 0 && r - kk < recent));
-                const int g0 = (kk / Mg) * Mg;
-                const int g1 = (g0 + Mg < Sk) ? g0 + Mg : Sk;
-                int rank = 0;
-                for (int k2 = g0; k2 < g1; ++k2)
-                    if (x[k2] > x[kk] || (x[k2] == x[kk] && k2 < kk)) ++rank;
-                keep[kk] = (unsigned char)(allowed && (dense || rank < N));
+            } else {
+                nm_keep_row(r, Sk, causal, N, Mg, sink, recent, x, keep);
             }
             for (int kk = 0; kk < Sk; ++kk)
                 if (keep[kk]) kw[kk >> 5] |= 1u << (kk & 31);
@@ -298,6 +307,162 @@ int oracle_nm_softmax(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
             lse_out[u * Br + rr] = mu + log(den);
         }
         free(x); free(keep); free(num);
+    }
+    return bad;
+}
+
+/* ------------------------------------------------------------------------------------------------
+ * Skip-softmax combined with N:M sparse softmax.  [MO-llm] "Custom Configuration" and the example
+ * script's skip_softmax_calib_sparse24 configuration (calibrated skip-softmax together with 2:4
+ * sparse softmax in one attention), with the two methods as above.  Reading: the N:M rule first
+ * fixes which keys of each query row may enter the softmax (the others become -inf); the
+ * skip-softmax loop then runs over the key tiles of those masked logits.  So, in order:
+ *
+ *   keep(r,k)  as in oracle_nm_softmax (ranking on raw scores q.k)
+ *   for each visited tile j in ascending order:
+ *     t[r][k] = c*q.k if keep(r,k) else -inf;  M_j[r] = max_k t[r][k]
+ *     skip iff every valid row has M_j[r] < m[r] + log2(lambda)   (m: running max of kept tiles)
+ *     kept tiles: the online-softmax update over their finite t.
+ *
+ * The group maximum always survives top-N (N >= 1), so M_j equals the tile max of the unmasked
+ * logits and the skip decisions equal those of skip-softmax alone.
+ *
+ * mode 0: double throughout.  mode 1 (replay): skip decisions from rowmax_in (fp32) as in
+ * oracle_skip_softmax and N:M ranks from scores_in [B,Hq,Sq,Sk] (fp32).  mode 2: tile states from
+ * state_in and keep bits from keep_in [B,Hq,Sq,W].  Outputs: o_out, lse_out, state_out and
+ * rowmax_out as oracle_skip_softmax (rowmax over the kept keys), keep_out [n_units][Br][W] as
+ * oracle_nm_softmax (the N:M keep bits, whatever the tile decision).
+ * ----------------------------------------------------------------------------------------------*/
+int oracle_skip_nm_softmax(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int Br,
+                           int Bc, double scale, double lambda, int N, int Mg, int sink, int recent,
+                           const uint16_t* q, const uint16_t* k, const uint16_t* v, int mode,
+                           const float* rowmax_in, const uint8_t* state_in, const float* scores_in,
+                           const uint32_t* keep_in, const int64_t* units, int64_t n_units,
+                           double* o_out, double* lse_out, uint8_t* state_out, double* rowmax_out,
+                           uint32_t* keep_out) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || Sq < 1 || Sk < 1 || D < 1 || Br < 1 || Bc < 1)
+        return 1;
+    if (causal && Sq != Sk) return 1;
+    if (!(lambda >= 0.0) || isinf(lambda)) return 1;
+    if (Mg < 1 || N < 1 || N > Mg || sink < 0 || recent < 0) return 1;
+    const int nQT = (Sq + Br - 1) / Br, nKT = (Sk + Bc - 1) / Bc, W = (Sk + 31) / 32;
+    const int group = Hq / Hkv;
+    const double c = scale * M_LOG2E;
+    const double L = (lambda == 0.0) ? -INFINITY : log2(lambda);
+    const float L32 = (lambda == 0.0) ? -INFINITY : (float)log2((double)(float)lambda);
+    int bad = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < n_units; ++u) {
+        const int64_t unit = units ? units[u] : u;
+        if (unit < 0 || unit >= (int64_t)B * Hq * nQT) { bad = 1; continue; }
+        const int i = (int)(unit % nQT);
+        const int hq = (int)((unit / nQT) % Hq);
+        const int b = (int)(unit / ((int64_t)nQT * Hq));
+        const int hk = hq / group;
+        const int r0 = i * Br, r1 = (r0 + Br < Sq) ? r0 + Br : Sq, nr = r1 - r0;
+
+        /* step 1: the N:M keep flags of every row of the query tile */
+        unsigned char* keep = calloc((size_t)Br * Sk, 1);
+        double* x = malloc(sizeof(double) * Sk);
+        for (int rr = 0; rr < Br; ++rr) {
+            uint32_t* kw = &keep_out[(u * Br + rr) * W];
+            for (int w = 0; w < W; ++w) kw[w] = 0u;
+            if (rr >= nr) continue;
+            const int r = r0 + rr;
+            const int64_t row = (((int64_t)b * Hq + hq) * Sq + r);
+            unsigned char* kr = &keep[(size_t)rr * Sk];
+            if (mode == 2) {
+                for (int kk = 0; kk < Sk; ++kk)
+                    kr[kk] = (unsigned char)((keep_in[row * W + (kk >> 5)] >> (kk & 31)) & 1u);
+            } else {
+                for (int kk = 0; kk < Sk; ++kk) {
+                    const int allowed = !causal || kk <= r;
+                    if (!allowed) x[kk] = -INFINITY;
+                    else if (mode == 1) x[kk] = (double)scores_in[row * Sk + kk];
+                    else x[kk] = dot_qk(q, k, Sq, Sk, Hq, Hkv, D, b, r, hq, kk, hk);
+                }
+                nm_keep_row(r, Sk, causal, N, Mg, sink, recent, x, kr);
+            }
+            for (int kk = 0; kk < Sk; ++kk)
+                if (kr[kk]) kw[kk >> 5] |= 1u << (kk & 31);
+        }
+
+        /* step 2: the skip-softmax loop over the masked logits */
+        double* m = malloc(sizeof(double) * Br);
+        double* l = malloc(sizeof(double) * Br);
+        float* m32 = malloc(sizeof(float) * Br);
+        double* acc = calloc((size_t)Br * D, sizeof(double));
+        double* t = malloc(sizeof(double) * Br * Bc);
+        double* M = malloc(sizeof(double) * Br);
+        for (int r = 0; r < Br; ++r) { m[r] = -INFINITY; l[r] = 0.0; m32[r] = -INFINITY; }
+
+        for (int j = 0; j < nKT; ++j) {
+            const int k0 = j * Bc, k1 = (k0 + Bc < Sk) ? k0 + Bc : Sk;
+            uint8_t* st = &state_out[u * nKT + j];
+            double* rm = &rowmax_out[(u * nKT + j) * Br];
+            for (int r = 0; r < Br; ++r) rm[r] = -INFINITY;
+            int visited = causal ? (k0 <= r1 - 1) : 1;
+            if (!visited) { *st = 2; continue; }
+            for (int rr = 0; rr < nr; ++rr) {
+                const int r = r0 + rr;
+                M[rr] = -INFINITY;
+                for (int kk = k0; kk < k1; ++kk) {
+                    double tv = -INFINITY;
+                    if (keep[(size_t)rr * Sk + kk])
+                        tv = c * dot_qk(q, k, Sq, Sk, Hq, Hkv, D, b, r, hq, kk, hk);
+                    t[rr * Bc + (kk - k0)] = tv;
+                    if (tv > M[rr]) M[rr] = tv;
+                }
+                rm[rr] = M[rr];
+            }
+            int skip;
+            if (mode == 2) {
+                skip = state_in[unit * nKT + j] == 1;
+            } else if (mode == 1) {
+                const float* Min = &rowmax_in[(unit * nKT + j) * Br];
+                skip = 1;
+                for (int rr = 0; rr < nr; ++rr)
+                    if (!(Min[rr] < (float)(m32[rr] + L32))) { skip = 0; break; }
+            } else {
+                skip = 1;
+                for (int rr = 0; rr < nr; ++rr)
+                    if (!(M[rr] < m[rr] + L)) { skip = 0; break; }
+            }
+            *st = (uint8_t)skip;
+            if (skip) continue;
+            for (int rr = 0; rr < nr; ++rr) {
+                if (mode == 1) {
+                    const float Mf = rowmax_in[(unit * nKT + j) * Br + rr];
+                    if (Mf > m32[rr]) m32[rr] = Mf;
+                }
+                const double m_new = (M[rr] > m[rr]) ? M[rr] : m[rr];
+                if (m_new == -INFINITY) continue;
+                const double alpha = (m[rr] == -INFINITY) ? 0.0 : exp2(m[rr] - m_new);
+                l[rr] *= alpha;
+                for (int e = 0; e < D; ++e) acc[rr * D + e] *= alpha;
+                for (int kk = k0; kk < k1; ++kk) {
+                    const double tv = t[rr * Bc + (kk - k0)];
+                    if (tv == -INFINITY) continue;
+                    const double p = exp2(tv - m_new);
+                    l[rr] += p;
+                    for (int e = 0; e < D; ++e)
+                        acc[rr * D + e] += p * at(v, Sk, Hkv, D, b, kk, hk, e);
+                }
+                m[rr] = m_new;
+            }
+        }
+        for (int rr = 0; rr < Br; ++rr) {
+            double* o = &o_out[(u * Br + rr) * D];
+            if (rr >= nr || l[rr] == 0.0) {
+                for (int e = 0; e < D; ++e) o[e] = 0.0;
+                lse_out[u * Br + rr] = (rr >= nr) ? 0.0 : -INFINITY;
+                continue;
+            }
+            for (int e = 0; e < D; ++e) o[e] = acc[rr * D + e] / l[rr];
+            lse_out[u * Br + rr] = (m[rr] + log2(l[rr])) * M_LN2;
+        }
+        free(keep); free(x); free(m); free(l); free(m32); free(acc); free(t); free(M);
     }
     return bad;
 }
