@@ -220,7 +220,27 @@ def run_paths(torch, sa, W, to_dev, steps, warmup):
     except sa.SaError as e:
         rec = {"unavailable": str(e)}
     out[wl.name] = rec
-    del qd, kd, vd, o
+
+    # skip-softmax with 2:4 inside kept tiles, same workload, lambda lowered from target 0.5
+    nQT, nKT = -(-S // wl.block_q), -(-S // wl.block_k)
+    st = torch.empty((B, H, nQT, nKT), dtype=torch.uint8, device=dev)
+    _, lam, _ = sa.sa_threshold_from_calib(W.CALIB_A, W.CALIB_B, 0.5, S)
+    P = tile_pairs(S, S, wl.block_q, wl.block_k, True)
+    rec = {"n:m": "2:4", "lambda": lam}
+    for name, lm in (("calibrated", lam), ("lambda0", 0.0)):
+        ms = time_steps(torch, lambda: sa.sa_skip_nm_softmax_fwd(
+            qd, kd, vd, o, lm, 2, 4, wl.param("sink"), wl.param("recent"), causal=True,
+            block_q=wl.block_q, block_k=wl.block_k, tile_state=st), steps, warmup)
+        ts = st.cpu().numpy()
+        comp, dense_eq = skip_flops(ts, P, D)
+        rec[name] = {"ms": round(ms, 4), "computed_tflops": round(comp / ms / 1e9, 2),
+                     "dense_equiv_tflops": round(dense_eq / ms / 1e9, 2),
+                     "tile_sparsity": round(float((ts == 1).sum() / max(1, (ts != 2).sum())), 4)}
+    rec["speedup_vs_lambda0"] = round(rec["lambda0"]["ms"] / rec["calibrated"]["ms"], 3)
+    if "2:4" in out[wl.name]:
+        rec["speedup_vs_nm_2:4"] = round(out[wl.name]["2:4"]["ms"] / rec["calibrated"]["ms"], 3)
+    out["llm_prefill_skip_nm_s4096"] = rec
+    del qd, kd, vd, o, st
 
     # proxy-compensated block-sparse attention with bitmask routes
     wl = W.WORKLOADS["proxy_bitmask_s16257"]

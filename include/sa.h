@@ -113,6 +113,28 @@ sa_status sa_nm_softmax_fwd(const sa_attn_desc* desc, const void* q, const void*
                             uint32_t* dbg_keep_bits, float* dbg_scores, void* stream);
 
 /*
+ * Skip-softmax and N:M sparse softmax in one forward (Model-Optimizer HuggingFace attention
+ * sparsity: the skip_softmax_calib_sparse24 configuration, calibrated skip-softmax together with
+ * 2:4 sparse softmax).  Reading: the N:M rule of sa_nm_softmax_fwd first fixes which keys of each
+ * query row may enter the softmax; the skip-softmax loop of sa_skip_softmax_fwd then runs over the
+ * tiles of those masked logits.  Top-n keeps every group maximum, so a tile's masked row maxima
+ * equal its unmasked ones and the skip decisions are exactly those of sa_skip_softmax_fwd at the
+ * same lambda; kept tiles contribute only their N:M-kept keys.
+ *
+ *   lambda, tile_state, head_counters, lse, dbg_tile_rowmax   as sa_skip_softmax_fwd.
+ *   (n, m), dense_sink_tokens, dense_recent_tokens, dbg_keep_bits, dbg_scores
+ *                     as sa_nm_softmax_fwd; dbg_keep_bits are the N:M bits of every visited
+ *                     tile, whether the tile was then kept or skipped.
+ * Supported: head_dim 64/128, block_q 64/128, block_k 64.
+ */
+sa_status sa_skip_nm_softmax_fwd(const sa_attn_desc* desc, const void* q, const void* k,
+                                 const void* v, void* o, float lambda, int32_t n, int32_t m,
+                                 int32_t dense_sink_tokens, int32_t dense_recent_tokens,
+                                 uint8_t* tile_state, uint32_t* head_counters, float* lse,
+                                 float* dbg_tile_rowmax, uint32_t* dbg_keep_bits,
+                                 float* dbg_scores, void* stream);
+
+/*
  * Route preparation, the "plan" step of the block-sparse path (FlashInfer proxy description,
  * "Bitmask format").  nKB = ceil(Sk/block_k), nQB = ceil(Sq/block_q), W = ceil(nKB/32).
  *

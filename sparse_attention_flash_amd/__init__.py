@@ -52,6 +52,9 @@ _lib.sa_skip_softmax_fwd.argtypes = [_DESC, _P, _P, _P, _P, _F, _P, _P, _P, _P, 
 _lib.sa_skip_softmax_fwd.restype = ctypes.c_int
 _lib.sa_nm_softmax_fwd.argtypes = [_DESC, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P]
 _lib.sa_nm_softmax_fwd.restype = ctypes.c_int
+_lib.sa_skip_nm_softmax_fwd.argtypes = [_DESC, _P, _P, _P, _P, _F, _I32, _I32, _I32, _I32, _P, _P,
+                                        _P, _P, _P, _P, _P]
+_lib.sa_skip_nm_softmax_fwd.restype = ctypes.c_int
 _lib.sa_bitmask_route_prep.argtypes = [_DESC, _P, _P, _P, _P, _P]
 _lib.sa_bitmask_route_prep.restype = ctypes.c_int
 _lib.sa_bsr_route_prep.argtypes = [_DESC, _P, _P, ctypes.c_int64, _P, _P, _P, _P, _P]
@@ -146,6 +149,19 @@ def sa_nm_softmax_fwd(q, k, v, o, n, m, dense_sink_tokens=0, dense_recent_tokens
                                   _ptr(lse), _ptr(dbg_keep_bits), _ptr(dbg_scores),
                                   _stream(stream)),
            "sa_nm_softmax_fwd")
+
+
+def sa_skip_nm_softmax_fwd(q, k, v, o, lam, n, m, dense_sink_tokens=0, dense_recent_tokens=0, *,
+                           causal=False, block_q=128, block_k=64, scale=None, tile_state=None,
+                           head_counters=None, lse=None, dbg_tile_rowmax=None, dbg_keep_bits=None,
+                           dbg_scores=None, stream=None):
+    d = make_desc(q, k, v, o, causal=causal, block_q=block_q, block_k=block_k, scale=scale)
+    _check(_lib.sa_skip_nm_softmax_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                       float(lam), int(n), int(m), int(dense_sink_tokens),
+                                       int(dense_recent_tokens), _ptr(tile_state),
+                                       _ptr(head_counters), _ptr(lse), _ptr(dbg_tile_rowmax),
+                                       _ptr(dbg_keep_bits), _ptr(dbg_scores), _stream(stream)),
+           "sa_skip_nm_softmax_fwd")
 
 
 def sa_bitmask_route_prep(bitmask, n_exact, exact_idx, proxy_keep, *, batch, heads_kv, seqlen_q,

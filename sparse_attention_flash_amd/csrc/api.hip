@@ -141,6 +141,34 @@ sa_status sa_nm_softmax_fwd(const sa_attn_desc* desc, const void* q, const void*
   return from_hip(sa::launch_nm_softmax(a, (hipStream_t)stream));
 }
 
+sa_status sa_skip_nm_softmax_fwd(const sa_attn_desc* desc, const void* q, const void* k,
+                                 const void* v, void* o, float lambda, int32_t n, int32_t m,
+                                 int32_t dense_sink_tokens, int32_t dense_recent_tokens,
+                                 uint8_t* tile_state, uint32_t* head_counters, float* lse,
+                                 float* dbg_tile_rowmax, uint32_t* dbg_keep_bits,
+                                 float* dbg_scores, void* stream) {
+  sa_status st = check_attention(desc, q, k, v, o);
+  if (st != SA_OK) return st;
+  if (desc->block_k != 64) return SA_ERR_UNSUPPORTED;
+  if (!((m == 4 && n >= 1 && n <= 4) || (m == 8 && n >= 1 && n <= 8))) return SA_ERR_UNSUPPORTED;
+  if (dense_sink_tokens < 0 || dense_recent_tokens < 0) return SA_ERR_VALUE;
+  if (!(lambda >= 0.f) || !std::isfinite(lambda)) return SA_ERR_VALUE;
+  sa::SkipNmArgs a{};
+  a.g = geometry(desc, q, k, v, o);
+  a.L32 = lambda == 0.f ? -INFINITY : (float)std::log2((double)lambda);
+  a.tile_state = tile_state;
+  a.counters = head_counters;
+  a.lse = lse;
+  a.rowmax = dbg_tile_rowmax;
+  a.n = n;
+  a.m = m;
+  a.sink = dense_sink_tokens;
+  a.recent = dense_recent_tokens;
+  a.keep_bits = dbg_keep_bits;
+  a.scores = dbg_scores;
+  return from_hip(sa::launch_skip_nm_softmax(a, (hipStream_t)stream));
+}
+
 sa_status sa_bitmask_route_prep(const sa_attn_desc* desc, const uint32_t* bitmask,
                                 int32_t* n_exact, int32_t* exact_idx, uint32_t* proxy_keep,
                                 void* stream) {

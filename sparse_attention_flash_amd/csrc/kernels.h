@@ -35,6 +35,19 @@ struct NmArgs {
   float* scores;
 };
 
+// skip-softmax with the N:M rule inside kept tiles: the fields of SkipArgs and NmArgs
+struct SkipNmArgs {
+  AttnGeom g;
+  float L32;
+  uint8_t* tile_state;
+  uint32_t* counters;
+  float* lse;
+  float* rowmax;
+  int n, m, sink, recent;
+  uint32_t* keep_bits;
+  float* scores;
+};
+
 struct RouteArgs {
   const uint32_t* bitmask;
   int32_t* n_exact;
@@ -72,6 +85,7 @@ struct ProxyArgs {
 
 hipError_t launch_skip_softmax(const SkipArgs& a, hipStream_t stream);
 hipError_t launch_nm_softmax(const NmArgs& a, hipStream_t stream);
+hipError_t launch_skip_nm_softmax(const SkipNmArgs& a, hipStream_t stream);
 hipError_t launch_route_prep(const RouteArgs& a, hipStream_t stream);
 hipError_t launch_bsr_route_prep(const BsrRouteArgs& a, hipStream_t stream);
 hipError_t launch_proxy(const ProxyArgs& a, hipStream_t stream);

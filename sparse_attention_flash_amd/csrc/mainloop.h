@@ -1,4 +1,5 @@
-// mainloop.h -- the pipelined key-tile loop shared by the skip-softmax, N:M and proxy kernels.
+// mainloop.h -- the pipelined key-tile loop shared by the skip-softmax, N:M, combined and proxy
+// kernels.
 //
 // One workgroup of NW wavefronts, each owning QB blocks of 32 query rows, walks a sequence of
 // 64-key tiles ("steps") given by a policy object.  K and V tiles are copied HBM/L2 -> LDS with
@@ -227,7 +228,7 @@ __device__ __forceinline__ void softmax_pv(const Pol& pol, int step, const f32x1
 //   bool negligible(const float (&M)[QB], const float (&mt)[QB], int lane) const;   [kDecide]
 //   void filter(int step, const f32x16 (&s)[2][QB], uint32_t (&bits)[QB], int lane) const; [kFilter]
 //   bool weighted(int step) const; float weight(int step, int kb, int r, int lane) const; [kWeighted]
-//   void record(int step, bool keep, const float (&M)[QB], int wave, int lane, int tid);
+//   void record(int step, bool keep, const float (&M)[QB], int wave, int lane, bool leader);
 // On return o, mref and l hold the unnormalised accumulator, exponent reference and row-sum
 // partials of this lane (l still to be summed over the two lane halves).
 template <int D, int NW, int QB, class Pol>
@@ -293,7 +294,7 @@ struct Mainloop {
       for (int qb = 0; qb < QB; ++qb) mt[qb] = fmaxf(mt[qb], ts.M[qb]);
       issue_v(step);
     }
-    pol.record(step, ts.keep, ts.M, wave, lane, tid);
+    pol.record(step, ts.keep, ts.M, wave, lane, tid == 0);
   }
 
   // iteration j.  On entry S(j) is in sa with keep(j) resolved (V(j) requested when kept), S(j+1)

@@ -1,0 +1,448 @@
+// policies.h -- the per-method parts of the key-tile loop (mainloop.h) and the kernel body shared
+// by the dense-walk kernels (skip-softmax, N:M, and the two combined).
+//
+//   KeyTiles      walks every visited 64-key tile of the query tile in order; causal and
+//                 out-of-range keys are masked to -inf.
+//   SkipDecision  the skip-softmax rule (Model-Optimizer "Skip-Softmax Sparse Attention for
+//                 Diffusion Models": a key tile whose scores are negligible under lambda is
+//                 skipped, saving its exponentials, V load and P.V; the kernel works with
+//                 log2(lambda)): tile j is skipped when every valid row r has
+//                 M_j[r] < fl32(m[r] + log2(lambda)), m the fp32 running max of the kept tiles.
+//   NmFilter      the N:M rule (Model-Optimizer "Attention Sparsity for HuggingFace Models",
+//                 "N:M Sparse Softmax": per query, of every M consecutive keys keep the top N,
+//                 the others -inf; sink and recent windows stay dense).
+//
+// A policy is KeyTiles plus any of the two rules; attention_tile() is the kernel body around it.
+#pragma once
+
+#include "kernels.h"
+#include "mainloop.h"
+
+namespace sa {
+
+// Where one workgroup sits: (batch, query head, query tile), and this wave's first row.
+struct TileUnit {
+  int b, hq, hk, qt, row0, wrow0, nvis, nQT, nKT;
+  int64_t unit;   // (b*Hq + hq)*nQT + qt
+};
+
+// Work item order: KV head major, then query tile, then the G query heads sharing the KV head, so
+// that concurrently running workgroups of one XCD read the same K/V tiles.  Causal: the longest
+// rows first.
+template <int NW, int QB>
+__device__ __forceinline__ TileUnit tile_unit(const AttnGeom& g, int wave) {
+  constexpr int BR = NW * 32 * QB;
+  TileUnit u;
+  u.nQT = (g.Sq + BR - 1) / BR;
+  u.nKT = (g.Sk + kKeysPerTile - 1) / kKeysPerTile;
+  const int G = g.Hq / g.Hkv;
+  int item = xcd_remap(blockIdx.x, g.B * g.Hq * u.nQT);
+  const int gq = item % G;
+  item /= G;
+  int qt = item % u.nQT;
+  item /= u.nQT;
+  u.hk = item % g.Hkv;
+  u.b = item / g.Hkv;
+  if (g.causal) qt = u.nQT - 1 - qt;
+  u.qt = qt;
+  u.hq = u.hk * G + gq;
+  u.row0 = qt * BR;
+  u.wrow0 = u.row0 + wave * 32 * QB;
+  const int last_row = min(u.row0 + BR, g.Sq) - 1;
+  u.nvis = g.causal ? min(u.nKT, last_row / kKeysPerTile + 1) : u.nKT;
+  u.unit = ((int64_t)u.b * g.Hq + u.hq) * u.nQT + qt;
+  return u;
+}
+
+template <int QB>
+struct KeyTiles {
+  static constexpr int RW = 32 * QB;   // rows per wave
+  const __bf16* kslab;
+  const __bf16* vslab;
+  int k_stride_b, v_stride_b, k_bytes, v_bytes;
+  int Sq, Sk, causal, wrow0, nvis, h, r32;
+
+  __device__ __forceinline__ void init_tiles(const AttnGeom& g, const TileUnit& u, int D,
+                                             int lane) {
+    kslab = (const __bf16*)g.k + u.b * g.ks[0] + u.hk * g.ks[2];
+    vslab = (const __bf16*)g.v + u.b * g.vs[0] + u.hk * g.vs[2];
+    k_stride_b = (int)(g.ks[1] * 2);
+    v_stride_b = (int)(g.vs[1] * 2);
+    k_bytes = (int)(((int64_t)(g.Sk - 1) * g.ks[1] + D) * 2);
+    v_bytes = (int)(((int64_t)(g.Sk - 1) * g.vs[1] + D) * 2);
+    Sq = g.Sq;
+    Sk = g.Sk;
+    causal = g.causal;
+    wrow0 = u.wrow0;
+    nvis = u.nvis;
+    h = lane >> 5;
+    r32 = lane & 31;
+  }
+
+  __device__ __forceinline__ int steps() const { return nvis; }
+
+  __device__ __forceinline__ TileSrc src(int j) const {
+    const int k0 = j * kKeysPerTile;
+    return TileSrc{kslab + (int64_t)k0 * (k_stride_b / 2), vslab + (int64_t)k0 * (v_stride_b / 2),
+                   max(0, k_bytes - k0 * k_stride_b), max(0, v_bytes - k0 * v_stride_b),
+                   k_stride_b, v_stride_b};
+  }
+
+  // key = k0 + 4*h + off(kb, r) with off a compile-time constant; masked when off >= lim
+  __device__ __forceinline__ void mask(int j, f32x16 (&s)[2][QB], int) const {
+    const int k0 = j * kKeysPerTile;
+    if (!((k0 + kKeysPerTile > Sk) || (causal && k0 + kKeysPerTile - 1 > wrow0))) return;
+    const int klim = Sk - k0 - 4 * h;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      int lim = klim;
+      if (causal) lim = min(lim, wrow0 + qb * 32 + r32 - k0 - 4 * h + 1);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) mask_block(s[kb][qb], kb, lim);
+    }
+  }
+
+  // defaults for a policy without the rule
+  __device__ __forceinline__ bool negligible(const float (&)[QB], const float (&)[QB], int) const {
+    return false;
+  }
+  __device__ __forceinline__ void filter(int, const f32x16 (&)[2][QB], uint32_t (&)[QB], int) const {}
+  __device__ __forceinline__ void record(int, bool, const float (&)[QB], int, int, bool) {}
+};
+
+// ---- the skip rule --------------------------------------------------------------------------------
+
+template <int D, int NW, int QB>
+struct SkipDecision : KeyTiles<QB> {
+  static constexpr bool kDecide = true, kFilter = false, kWeighted = false;
+  static constexpr int RW = 32 * QB;
+  static constexpr int BR = NW * RW;
+  float L32;
+  uint8_t* tile_state;
+  float* rowmax;
+  int64_t unit;
+  int nKT, nskip;
+
+  // Args: SkipArgs or SkipNmArgs
+  template <class Args>
+  __device__ __forceinline__ void init(const Args& a, const TileUnit& u, int lane) {
+    this->init_tiles(a.g, u, D, lane);
+    nKT = u.nKT;
+    L32 = a.L32;
+    tile_state = a.tile_state;
+    rowmax = a.rowmax;
+    unit = u.unit;
+    nskip = 0;
+  }
+
+  // true when every valid row this lane holds is negligible: M < fl32(m + log2(lambda))
+  __device__ __forceinline__ bool negligible(const float (&M)[QB], const float (&mt)[QB],
+                                             int) const {
+    bool negl = true;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float thr = mt[qb] + L32;
+      if (this->wrow0 + qb * 32 + this->r32 < this->Sq && !(M[qb] < thr)) negl = false;
+    }
+    return negl;
+  }
+
+  __device__ __forceinline__ void record(int j, bool keep, const float (&M)[QB], int wave, int,
+                                         bool leader) {
+    if (!keep) ++nskip;
+    if (leader && tile_state != nullptr) tile_state[unit * nKT + j] = keep ? 0 : 1;
+    if (rowmax != nullptr && this->h == 0) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        rowmax[(unit * nKT + j) * BR + wave * RW + qb * 32 + this->r32] = M[qb];
+    }
+  }
+
+  // tiles never visited (causal): state 2, maxima -inf; the head counters
+  template <class Args>
+  __device__ __forceinline__ void finish(const Args& a, const TileUnit& u, int tid) const {
+    constexpr int NT = NW * 64;
+    if (a.tile_state != nullptr)
+      for (int j = u.nvis + tid; j < nKT; j += NT) a.tile_state[unit * nKT + j] = 2;
+    if (a.rowmax != nullptr)
+      for (int64_t i = (int64_t)u.nvis * BR + tid; i < (int64_t)nKT * BR; i += NT)
+        a.rowmax[unit * nKT * BR + i] = -INFINITY;
+    if (tid == 0 && a.counters != nullptr) {
+      atomicAdd(&a.counters[2 * (u.b * a.g.Hq + u.hq)], (unsigned)u.nvis);
+      atomicAdd(&a.counters[2 * (u.b * a.g.Hq + u.hq) + 1], (unsigned)nskip);
+    }
+  }
+};
+
+// ---- the N:M rule ---------------------------------------------------------------------------------
+// In the S^T register layout a lane holds, for one query, keys 8g + 4h + {0..3} in elements
+// 4g..4g+3 (h = lane/32), so an M = 4 group is four consecutive elements of one lane and an M = 8
+// group is those four plus the same four elements of lane ^ 32 (one v_permlane32_swap).  Dropped
+// keys get weight 0 in P.  The running max needs no change: the group maximum always survives
+// (rank 0 < N), so the max over kept keys equals the max over allowed keys -- which is also why
+// the skip rule may be decided on the unfiltered tile maxima.
+
+// 1 when d < 0, else 0, for d the fp32 difference of two finite scores normalised by "+ 0.0f"
+// (so that equal scores give +0): the sign bit, read without a compare (a compare per pair would
+// park a lane mask in SGPRs).
+__device__ __forceinline__ int neg01(float d) { return (int)(__float_as_uint(d + 0.0f) >> 31); }
+
+// rank[i] = number of group members that beat own[i]: a higher score, or an equal score at a lower
+// key index.  own[0..3] are this lane's four keys in ascending key order; for M = 8, oth[0..3] are
+// the lane ^ 32 half of the group, whose keys all come after ours when own_first is true.  Scores
+// are finite here (masked keys enter as -FLT_MAX, which still ties only with other masked keys).
+template <int M>
+__device__ __forceinline__ void group_ranks(const float (&own)[4], const float (&oth)[4],
+                                            bool own_first, int (&rank)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rank[i] = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = i + 1; j < 4; ++j) {
+      // j comes after i: j beats i iff own[j] > own[i], otherwise i beats j
+      const int jgt = neg01(own[i] - own[j]);
+      rank[i] += jgt;
+      rank[j] += 1 - jgt;
+    }
+  if constexpr (M == 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // other half after ours: it beats own[i] iff strictly greater; before ours: iff >=
+        const int gt = neg01(own[i] - oth[j]);   // oth[j] > own[i]
+        const int lt = neg01(oth[j] - own[i]);   // oth[j] < own[i]
+        rank[i] += own_first ? gt : 1 - lt;
+      }
+  }
+}
+
+// This lane's 32 keys of a 64-key tile, bit b = kb*16 + r, sit at key offsets
+// p(b) = kb*32 + (r/4)*8 + 4h + r%4, which increase with b: the keys with offset < T are the
+// low bits, as many as there are such offsets.
+__device__ __forceinline__ uint32_t bits_below(int T, int h) {
+  int cnt = 0;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cnt += min(max(T - (kb * 32 + q * 8 + 4 * h), 0), 4);
+  return cnt >= 32 ? 0xFFFFFFFFu : ((1u << cnt) - 1u);
+}
+
+template <int NW, int QB, int M>
+struct NmFilter {
+  static constexpr int RW = 32 * QB;
+  static constexpr int BR = NW * RW;
+  int n, sink, recent, W;
+  uint32_t* keep_bits;
+  float* scores;
+  int64_t row_base;   // (b*Hq + hq)*Sq
+
+  // Args: NmArgs or SkipNmArgs
+  template <class Args>
+  __device__ __forceinline__ void init(const Args& a, const TileUnit& u) {
+    n = a.n;
+    sink = a.sink;
+    recent = a.recent;
+    W = (a.g.Sk + 31) / 32;
+    keep_bits = a.keep_bits;
+    scores = a.scores;
+    row_base = ((int64_t)u.b * a.g.Hq + u.hq) * a.g.Sq;
+  }
+
+  // keep bit (kb*16 + r) of bits[qb]: key not masked and (dense, or top-n of its group).  The
+  // ranks are sign-bit arithmetic per element; the sink/recent windows and masked keys are key
+  // ranges, turned into bit ranges (bits_below) on the few tiles per row that touch them.
+  __device__ __forceinline__ void filter(const KeyTiles<QB>& kt, int j, const f32x16 (&s)[2][QB],
+                                         uint32_t (&bits)[QB], int lane) const {
+    const int k0 = j * kKeysPerTile;
+    const int Sk = kt.Sk, wrow0 = kt.wrow0, h = kt.h;
+    const bool any_masked =
+        (k0 + kKeysPerTile > Sk) || (kt.causal && k0 + kKeysPerTile - 1 > wrow0);
+    const bool any_dense = k0 < sink ||
+        (recent > 0 && k0 <= wrow0 + RW - 1 && k0 + kKeysPerTile - 1 > wrow0 - recent);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = wrow0 + qb * 32 + kt.r32;
+      uint32_t kb_bits = 0u;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          float own[4], oth[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            own[e] = fmaxf(s[kb][qb][4 * gi + e], -3.402823466e38f);   // masked: finite sentinel
+            oth[e] = own[e];
+            if constexpr (M == 8) oth[e] = other_half(own[e], lane);
+          }
+          int rank[4];
+          group_ranks<M>(own, oth, h == 0, rank);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)   // top-n: rank - n < 0
+            kb_bits |= ((uint32_t)(rank[e] - n) >> 31) << (kb * 16 + 4 * gi + e);
+          // one group at a time: the scheduler would otherwise interleave all eight groups'
+          // comparisons and run out of registers
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (any_dense) {   // key < sink, or row - recent < key <= row
+        kb_bits |= bits_below(sink - k0, h);
+        if (recent > 0) kb_bits |= bits_below(row - k0 + 1, h) & ~bits_below(row - recent - k0 + 1, h);
+      }
+      if (any_masked)    // key < Sk and (causal) key <= row
+        kb_bits &= bits_below(kt.causal ? min(Sk, row + 1) - k0 : Sk - k0, h);
+      bits[qb] = kb_bits;
+      if (keep_bits != nullptr || scores != nullptr) export_row(kt, k0, row, qb, kb_bits, s, lane);
+    }
+  }
+
+  // debug exports of one query row: keep-bit words and raw scores
+  __device__ __forceinline__ void export_row(const KeyTiles<QB>& kt, int k0, int row, int qb,
+                                             uint32_t kb_bits, const f32x16 (&s)[2][QB],
+                                             int lane) const {
+    // lanes l and l^32 hold the same row: both stay active through the swap
+    const int64_t rbase = row_base + row;
+    const int Sk = kt.Sk, h = kt.h;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      // this lane's 16 bits sit at key offsets (r/4)*8 + 4h + r%4: spread the nibbles 8 apart,
+      // then shift by 4h; merged with lane^32's half
+      const uint32_t x = (kb_bits >> (kb * 16)) & 0xFFFFu;
+      uint32_t word = ((x & 0xFu) | ((x & 0xF0u) << 4) | ((x & 0xF00u) << 8) |
+                       ((x & 0xF000u) << 12)) << (4 * h);
+      word |= __float_as_uint(other_half(__uint_as_float(word), lane));
+      if (row < kt.Sq) {
+        if (keep_bits != nullptr && h == 0 && k0 + kb * 32 < Sk)
+          keep_bits[rbase * W + k0 / 32 + kb] = word;
+        if (scores != nullptr) {
+          int kbase = k0 + 4 * h;   // key = kbase + c, c a compile-time constant
+          asm volatile("" : "+v"(kbase));
+          float* dst = scores + rbase * Sk + kbase;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+            if (kbase + c < Sk) dst[c] = s[kb][qb][r];
+          }
+        }
+      }
+    }
+  }
+
+  // keep-bit words and scores of tiles never visited (causal): zero / -inf
+  template <class Args>
+  __device__ __forceinline__ void finish(const Args& a, const TileUnit& u, int tid) const {
+    constexpr int NT = NW * 64;
+    const AttnGeom& g = a.g;
+    if (keep_bits != nullptr) {
+      const int wfirst = u.nvis * (kKeysPerTile / 32);
+      for (int rr = tid; rr < BR; rr += NT) {
+        const int row = u.row0 + rr;
+        if (row >= g.Sq) continue;
+        const int64_t rbase = row_base + row;
+        for (int w = wfirst; w < W; ++w) keep_bits[rbase * W + w] = 0u;
+      }
+    }
+    if (scores != nullptr) {
+      const int kfirst = u.nvis * kKeysPerTile;
+      for (int rr = 0; rr < BR; ++rr) {
+        const int row = u.row0 + rr;
+        if (row >= g.Sq) break;
+        const int64_t rbase = row_base + row;
+        for (int key = kfirst + tid; key < g.Sk; key += NT) scores[rbase * g.Sk + key] = -INFINITY;
+      }
+    }
+  }
+};
+
+// ---- the policies -----------------------------------------------------------------------------------
+
+template <int D, int NW, int QB>
+using SkipPolicy = SkipDecision<D, NW, QB>;
+
+template <int D, int NW, int QB, int M>
+struct NmPolicy : KeyTiles<QB> {
+  static constexpr bool kDecide = false, kFilter = true, kWeighted = false;
+  NmFilter<NW, QB, M> nm;
+
+  __device__ __forceinline__ void init(const NmArgs& a, const TileUnit& u, int lane) {
+    this->init_tiles(a.g, u, D, lane);
+    nm.init(a, u);
+  }
+  __device__ __forceinline__ void filter(int j, const f32x16 (&s)[2][QB], uint32_t (&bits)[QB],
+                                         int lane) const {
+    nm.filter(*this, j, s, bits, lane);
+  }
+  __device__ __forceinline__ void finish(const NmArgs& a, const TileUnit& u, int tid) const {
+    nm.finish(a, u, tid);
+  }
+};
+
+// Both rules: the skip decision on the tile maxima (equal to the maxima over the N:M-kept keys),
+// the N:M bits inside every kept tile.
+template <int D, int NW, int QB, int M>
+struct SkipNmPolicy : SkipDecision<D, NW, QB> {
+  static constexpr bool kDecide = true, kFilter = true, kWeighted = false;
+  NmFilter<NW, QB, M> nm;
+
+  __device__ __forceinline__ void init(const SkipNmArgs& a, const TileUnit& u, int lane) {
+    SkipDecision<D, NW, QB>::init(a, u, lane);
+    nm.init(a, u);
+  }
+  __device__ __forceinline__ void filter(int j, const f32x16 (&s)[2][QB], uint32_t (&bits)[QB],
+                                         int lane) const {
+    nm.filter(*this, j, s, bits, lane);
+  }
+  __device__ __forceinline__ void finish(const SkipNmArgs& a, const TileUnit& u, int tid) const {
+    SkipDecision<D, NW, QB>::finish(a, u, tid);
+    nm.finish(a, u, tid);
+  }
+};
+
+// ---- the kernel body ----------------------------------------------------------------------------------
+// One workgroup = one (batch, query head, query tile of 32*QB*NW rows); each wavefront owns 32*QB
+// rows.  Load Q, run the key-tile loop with the policy, then normalise and store O and the
+// natural-log LSE.
+template <int D, int NW, int QB, class Pol, class Args>
+__device__ __forceinline__ void attention_tile(const Args& a, Smem<D, NW>& sm) {
+  const AttnGeom& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, r32 = lane & 31;
+  const TileUnit u = tile_unit<NW, QB>(g, wave);
+
+  const auto qsrc = slab_rsrc((const __bf16*)g.q + u.b * g.qs[0] + u.hq * g.qs[2], g.qs[1], g.Sq, D);
+  bf16x8 qf[QB][D / 16];
+  load_q_frags<D, QB>(qf, qsrc, g.qs[1], u.wrow0, lane);
+
+  Pol pol;
+  pol.init(a, u, lane);
+
+  f32x16 o[D / 32][QB];
+  float mref[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db][qb] = f32x16{};
+    mref[qb] = -INFINITY;
+    l[qb] = 0.f;
+  }
+  run_mainloop<D, NW, QB>(pol, sm, qf, o, mref, l, g.c32, wave, lane, tid);
+  pol.finish(a, u, tid);
+
+  float inv[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = half_sum(l[qb]);
+    inv[qb] = lt > 0.f ? 1.f / lt : 0.f;
+    const int row = u.wrow0 + qb * 32 + r32;
+    if (a.lse != nullptr && h == 0 && row < g.Sq)
+      a.lse[((int64_t)u.b * g.Hq + u.hq) * g.Sq + row] =
+          lt > 0.f ? (mref[qb] + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
+  }
+  __bf16* op = (__bf16*)g.o + u.b * g.os[0] + (int64_t)u.wrow0 * g.os[1] + u.hq * g.os[2];
+  store_o<D, QB>(op, g.os[1], g.Sq - u.wrow0, o, inv, lane);
+}
+
+}  // namespace sa

@@ -58,7 +58,7 @@ struct ExactPolicy {
     return false;
   }
   __device__ __forceinline__ void filter(int, const f32x16 (&)[2][QB], uint32_t (&)[QB], int) const {}
-  __device__ __forceinline__ void record(int, bool, const float (&)[QB], int, int, int) {}
+  __device__ __forceinline__ void record(int, bool, const float (&)[QB], int, int, bool) {}
 };
 
 // Proxy tiles: 64 summary rows at a time; rows whose proxy_keep bit is clear (or past nKB) are

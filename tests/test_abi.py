@@ -26,7 +26,9 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol():
     names = declared_entry_points()
-    assert {"sa_skip_softmax_fwd", "sa_nm_softmax_fwd", "sa_bitmask_route_prep", "sa_bsr_route_prep",
+    assert {"sa_skip_softmax_fwd", "sa_nm_softmax_fwd", "sa_skip_nm_softmax_fwd",
+            "sa_bitmask_route_prep", "sa_bsr_route_prep", "sa_skip_softmax_calibrate",
+            "sa_fit_threshold_calib",
             "sa_proxy_block_sparse_fwd", "sa_threshold_from_calib", "sa_status_str"} <= set(names)
     lib = ctypes.CDLL(sa.LIB_PATH)
     for n in names:
@@ -182,3 +184,20 @@ def test_calibrate_rejects():
     assert call([float("nan")]) == sa.SA_ERR_VALUE
     assert call([0.1], desc=None) == sa.SA_ERR_NULL
     assert call([0.1], desc=_desc(block_k=128)) == sa.SA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("lam,n,m,sink,recent,code", [
+    (-1.0, 2, 4, 0, 0, "VALUE"), (float("inf"), 2, 4, 0, 0, "VALUE"),
+    (0.1, 5, 4, 0, 0, "UNSUPPORTED"), (0.1, 0, 4, 0, 0, "UNSUPPORTED"), (0.1, 2, 6, 0, 0, "UNSUPPORTED"),
+    (0.1, 2, 4, -1, 0, "VALUE"), (0.1, 2, 4, 0, -1, "VALUE")])
+def test_skip_nm_rejects(lam, n, m, sink, recent, code):
+    d = _desc()
+    f = sa.raw.sa_skip_nm_softmax_fwd
+    got = f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, lam, n, m, sink, recent, None, None, None,
+            None, None, None, None)
+    assert got == getattr(sa, "SA_ERR_" + code)
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 0.1, 2, 4, 0, 0, None, None, None, None, None, None,
+             None) == sa.SA_ERR_NULL
+    d64 = _desc(block_k=128)
+    assert f(ctypes.byref(d64), FAKE, FAKE, FAKE, FAKE, 0.1, 2, 4, 0, 0, None, None, None, None,
+             None, None, None) == sa.SA_ERR_UNSUPPORTED
