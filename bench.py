@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (no sparsity)
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 HEADLINE = "video_dit_s32760"
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -242,6 +243,12 @@ def run_paths(torch, sa, W, to_dev, steps, warmup):
     out["llm_prefill_skip_nm_s4096"] = rec
     del qd, kd, vd, o, st
 
+    # decode step: one query per head against a ragged KV cache (HBM-bound)
+    try:
+        out["llm_decode_gqa_kv8192"] = decode_path(torch, sa, W, to_dev, steps, warmup)
+    except sa.SaError as e:
+        out["llm_decode_gqa_kv8192"] = {"unavailable": str(e)}
+
     # proxy-compensated block-sparse attention with bitmask routes
     wl = W.WORKLOADS["proxy_bitmask_s16257"]
     q, k, v = wl.generate()
@@ -282,6 +289,62 @@ def run_paths(torch, sa, W, to_dev, steps, warmup):
         rec["unavailable"] = str(e)
     out[wl.name] = rec
     return out
+
+
+def decode_path(torch, sa, W, to_dev, steps, warmup):
+    """Decode skip-softmax at the pages' decode threshold, at a threshold calibrated for 50 %
+    tile sparsity, and at lambda = 0, with its HBM roofline (algorithmic bytes: K of every visited
+    key, V of every key in a tile kept by some head of its KV group, q and o)."""
+    wl = W.WORKLOADS["llm_decode_gqa_kv8192"]
+    q, k, v, lens = wl.generate()
+    B, _, Hq, D = q.shape
+    S, Hkv = k.shape[1], k.shape[2]
+    G, BC = Hq // Hkv, wl.block_k
+    nKT = -(-S // BC)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o = torch.empty_like(qd)
+    ln = torch.from_numpy(lens).to(dev)
+    st = torch.empty((B, Hq, nKT), dtype=torch.uint8, device=dev)
+    cnt = torch.zeros((B, Hq, 2), dtype=torch.int32, device=dev)
+    nbytes, _ = sa.sa_skip_softmax_decode_workspace(qd, kd, 1.0, block_k=BC)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    kw = dict(block_k=BC, seqlens_k=ln, workspace=ws)
+
+    def sparsity_at(lam):
+        cnt.zero_()
+        sa.sa_skip_softmax_decode_fwd(qd, kd, vd, o, lam, head_counters=cnt, **kw)
+        c = cnt.cpu().numpy().astype(np.int64)
+        return float(c[..., 1].sum() / max(1, c[..., 0].sum()))
+
+    trials = [t for t in W.THRESHOLD_TRIALS if t <= 1.0]
+    sp = [sparsity_at(t) for t in trials]
+    rec = {"batch": B, "heads_q": Hq, "heads_kv": Hkv, "cache": S, "keys": int(lens.sum()),
+           "tile": BC, "calibration": {"trials": trials, "sparsity": [round(x, 4) for x in sp]}}
+    try:
+        a, b, lo, hi = sa.sa_fit_threshold_calib(trials, sp, S)
+        lam_cal = min(1.0, sa.sa_threshold_from_calib(a, b, wl.param("target_sparsity"), S)[1])
+        rec["calibration"].update({"fit_a": a, "fit_b": b, "fit_range": [lo, hi]})
+    except sa.SaError:
+        lam_cal = 1.0   # no usable trials: the largest threshold that keeps the split exact
+    keys_b = lens.astype(np.int64)
+    qo_bytes = 2 * B * Hq * D * 2
+    for name, lam in (("lambda_page", wl.param("lambda")), ("calibrated", lam_cal),
+                      ("lambda0", 0.0)):
+        ms = time_steps(torch, lambda: sa.sa_skip_softmax_decode_fwd(
+            qd, kd, vd, o, lam, tile_state=st, **kw), steps, warmup)
+        ts = st.cpu().numpy().reshape(B, Hkv, G, nKT)
+        kept_any = (ts == 0).any(axis=2)                                   # [B, Hkv, nKT]
+        tile_keys = np.clip(keys_b[:, None] - np.arange(nKT)[None, :] * BC, 0, BC)   # [B, nKT]
+        k_bytes = int(keys_b.sum()) * Hkv * D * 2
+        v_bytes = int((kept_any * tile_keys[:, None, :]).sum()) * D * 2
+        alg = k_bytes + v_bytes + qo_bytes
+        rec[name] = {"lambda": lam, "ms": round(ms, 4),
+                     "tile_sparsity": round(float((ts == 1).sum() / max(1, (ts != 2).sum())), 4),
+                     "alg_bytes": alg, "gbps": round(alg / ms / 1e6, 1),
+                     "hbm_frac": round(alg / ms / 1e6 / PEAK_HBM_GBPS, 4)}
+    rec["speedup_calibrated_vs_lambda0"] = round(rec["lambda0"]["ms"] / rec["calibrated"]["ms"], 3)
+    return rec
 
 
 # ------------------------------------------------------------------------------------------------

@@ -33,6 +33,7 @@
 #ifndef SA_H
 #define SA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -133,6 +134,48 @@ sa_status sa_skip_nm_softmax_fwd(const sa_attn_desc* desc, const void* q, const 
                                  uint8_t* tile_state, uint32_t* head_counters, float* lse,
                                  float* dbg_tile_rowmax, uint32_t* dbg_keep_bits,
                                  float* dbg_scores, void* stream);
+
+/*
+ * Decode-phase skip-softmax forward: one query token per (batch, query head) against a KV cache
+ * (Model-Optimizer skip-softmax rule as in sa_skip_softmax_fwd, used in the decode phase with its
+ * own threshold: the HuggingFace attention-sparsity configuration gives phase-specific thresholds,
+ * decode 1e-4).  The query tile is the single query row, so with t = softmax_scale*log2(e)*q.k the
+ * key tile j of head h is skipped when
+ *     M_j < fl32(m + L),   L = (float)log2((double)lambda),
+ * m the fp32 running max of the tiles kept so far -- sa_skip_softmax_fwd with seqlen_q = 1 and a
+ * one-row query tile, evaluated independently per query head.
+ *
+ * The key axis is split over workgroups.  For lambda <= 1 this is exact: a skipped tile could not
+ * have raised the running max, so each split starts from the max of all earlier tile maxima.  For
+ * lambda > 1 the decisions depend on the order of the kept tiles and the call runs one split
+ * (num_splits > 1 is then SA_ERR_UNSUPPORTED).
+ *
+ *   desc              seqlen_q == 1 and causal == 0 (SA_ERR_UNSUPPORTED otherwise); seqlen_k is the
+ *                     cache capacity; block_k 64 or 128 is the decision tile; block_q is ignored.
+ *                     heads_q/heads_kv <= 16 (head_dim 128) or <= 8 (head_dim 64).
+ *   q, o              [B, 1, Hq, D] (strides as in the descriptor); k, v [B, Sk, Hkv, D].
+ *   seqlens_k         optional device int32 [B]: keys of each sequence, clamped to [0, Sk]; NULL
+ *                     means Sk for all.  Tiles past a sequence's end are not visited (state 2); a
+ *                     sequence of 0 keys gets O = 0 and lse = -inf.
+ *   num_splits        0 picks a split count; otherwise the number of key-axis splits.
+ *   workspace         device memory of at least sa_skip_softmax_decode_workspace bytes for the
+ *                     same desc, lambda and num_splits, 256-byte aligned; contents are scratch.
+ *   tile_state        optional uint8 [B, Hq, nKT]: 0 kept, 1 skipped, 2 not visited.
+ *   head_counters     optional uint32 [B, Hq, 2] {visited, skipped}, added to.
+ *   lse               optional fp32 [B, Hq].
+ *   dbg_tile_rowmax   optional fp32 [B, Hq, nKT]: the M_j used (log2 domain), -inf when not
+ *                     visited.
+ * Three kernels on the stream: scores and tile maxima, decisions and P.V over kept tiles, merge.
+ */
+sa_status sa_skip_softmax_decode_workspace(const sa_attn_desc* desc, float lambda,
+                                           int32_t num_splits, size_t* workspace_bytes,
+                                           int32_t* num_splits_used);
+sa_status sa_skip_softmax_decode_fwd(const sa_attn_desc* desc, const void* q, const void* k,
+                                     const void* v, void* o, float lambda,
+                                     const int32_t* seqlens_k, int32_t num_splits,
+                                     void* workspace, size_t workspace_bytes,
+                                     uint8_t* tile_state, uint32_t* head_counters, float* lse,
+                                     float* dbg_tile_rowmax, void* stream);
 
 /*
  * Route preparation, the "plan" step of the block-sparse path (FlashInfer proxy description,

@@ -55,6 +55,11 @@ _lib.sa_nm_softmax_fwd.restype = ctypes.c_int
 _lib.sa_skip_nm_softmax_fwd.argtypes = [_DESC, _P, _P, _P, _P, _F, _I32, _I32, _I32, _I32, _P, _P,
                                         _P, _P, _P, _P, _P]
 _lib.sa_skip_nm_softmax_fwd.restype = ctypes.c_int
+_lib.sa_skip_softmax_decode_workspace.argtypes = [_DESC, _F, _I32, _P, _P]
+_lib.sa_skip_softmax_decode_workspace.restype = ctypes.c_int
+_lib.sa_skip_softmax_decode_fwd.argtypes = [_DESC, _P, _P, _P, _P, _F, _P, _I32, _P, ctypes.c_size_t,
+                                            _P, _P, _P, _P, _P]
+_lib.sa_skip_softmax_decode_fwd.restype = ctypes.c_int
 _lib.sa_bitmask_route_prep.argtypes = [_DESC, _P, _P, _P, _P, _P]
 _lib.sa_bitmask_route_prep.restype = ctypes.c_int
 _lib.sa_bsr_route_prep.argtypes = [_DESC, _P, _P, ctypes.c_int64, _P, _P, _P, _P, _P]
@@ -162,6 +167,33 @@ def sa_skip_nm_softmax_fwd(q, k, v, o, lam, n, m, dense_sink_tokens=0, dense_rec
                                        _ptr(head_counters), _ptr(lse), _ptr(dbg_tile_rowmax),
                                        _ptr(dbg_keep_bits), _ptr(dbg_scores), _stream(stream)),
            "sa_skip_nm_softmax_fwd")
+
+
+def sa_skip_softmax_decode_workspace(q, k, lam, *, block_k=64, num_splits=0, scale=None):
+    """(workspace bytes, splits used) for a decode call with these shapes."""
+    d = make_desc(q, k, block_q=64, block_k=block_k, scale=scale)
+    nbytes, used = ctypes.c_size_t(), ctypes.c_int32()
+    _check(_lib.sa_skip_softmax_decode_workspace(ctypes.byref(d), float(lam), int(num_splits),
+                                                 ctypes.addressof(nbytes), ctypes.addressof(used)),
+           "sa_skip_softmax_decode_workspace")
+    return nbytes.value, used.value
+
+
+def sa_skip_softmax_decode_fwd(q, k, v, o, lam, *, block_k=64, seqlens_k=None, num_splits=0,
+                               workspace=None, scale=None, tile_state=None, head_counters=None,
+                               lse=None, dbg_tile_rowmax=None, stream=None):
+    """q, o [B, 1, Hq, D]; k, v [B, Sk, Hkv, D].  Without a workspace one is allocated."""
+    d = make_desc(q, k, v, o, block_q=64, block_k=block_k, scale=scale)
+    if workspace is None:
+        nbytes, _ = sa_skip_softmax_decode_workspace(q, k, lam, block_k=block_k,
+                                                     num_splits=num_splits, scale=scale)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _check(_lib.sa_skip_softmax_decode_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                           float(lam), _ptr(seqlens_k), int(num_splits),
+                                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                           _ptr(tile_state), _ptr(head_counters), _ptr(lse),
+                                           _ptr(dbg_tile_rowmax), _stream(stream)),
+           "sa_skip_softmax_decode_fwd")
 
 
 def sa_bitmask_route_prep(bitmask, n_exact, exact_idx, proxy_keep, *, batch, heads_kv, seqlen_q,

@@ -4,6 +4,7 @@
 // writes nothing, which also lets the checks be exercised on a machine without a GPU.  Accepted
 // calls are lowered into the plain launch structs of kernels.h (the user-facing description is
 // not passed to the kernels) and enqueued on the caller's stream.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <vector>
@@ -84,6 +85,62 @@ sa::AttnGeom geometry(const sa_attn_desc* d, const void* q, const void* k, const
 }
 
 sa_status from_hip(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
+
+// Decode: split plan and workspace layout, the same for the size query and the call.
+struct DecodePlan {
+  int GM, nKT, nsplit, tps;
+  size_t off_scores, off_tmax, off_pm, off_pl, off_po, bytes;
+};
+
+sa_status plan_decode(const sa_attn_desc* d, float lambda, int32_t num_splits, DecodePlan* p) {
+  if (d->seqlen_q != 1 || d->causal != 0) return SA_ERR_UNSUPPORTED;
+  if (d->block_k != 64 && d->block_k != 128) return SA_ERR_UNSUPPORTED;
+  if (!(lambda >= 0.f) || !std::isfinite(lambda)) return SA_ERR_VALUE;
+  if (num_splits < 0) return SA_ERR_VALUE;
+  const int G = d->heads_q / d->heads_kv;
+  const int gmax = d->head_dim == 128 ? 16 : 8;   // one writer lane per head in a key row
+  if (G > gmax) return SA_ERR_UNSUPPORTED;
+  p->GM = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
+  p->nKT = (int)(((int64_t)d->seqlen_k + d->block_k - 1) / d->block_k);
+  const int64_t units = (int64_t)d->batch * d->heads_kv;
+  int ns;
+  if (lambda > 1.f) {
+    // decisions depend on the order of the kept tiles: one split walks them all
+    if (num_splits > 1) return SA_ERR_UNSUPPORTED;
+    ns = 1;
+  } else if (num_splits > 0) {
+    ns = num_splits;
+  } else {
+    // about four workgroups per compute unit
+    ns = (int)std::min<int64_t>(std::max<int64_t>(1, (1024 + units - 1) / units), p->nKT);
+  }
+  ns = std::min(ns, p->nKT);
+  int tps = (p->nKT + ns - 1) / ns;
+  if (tps > sa::kMaxTilesPerSplit) {
+    if (lambda > 1.f || num_splits > 0) return SA_ERR_UNSUPPORTED;
+    tps = sa::kMaxTilesPerSplit;
+  }
+  p->tps = tps;
+  p->nsplit = (p->nKT + tps - 1) / tps;
+  if (units * p->nsplit > INT32_MAX) return SA_ERR_SHAPE;
+  const auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t heads = (size_t)d->batch * d->heads_q;
+  size_t off = 0;
+  p->off_scores = off;
+  off += up((size_t)units * d->seqlen_k * p->GM * sizeof(float));
+  p->off_tmax = off;
+  off += up(heads * p->nKT * sizeof(float));
+  p->off_pm = off;
+  off += up(heads * p->nsplit * sizeof(float));
+  p->off_pl = off;
+  off += up(heads * p->nsplit * sizeof(float));
+  p->off_po = off;
+  off += up(heads * p->nsplit * d->head_dim * sizeof(float));
+  p->bytes = off;
+  return SA_OK;
+}
+
+
 
 }  // namespace
 
@@ -167,6 +224,60 @@ sa_status sa_skip_nm_softmax_fwd(const sa_attn_desc* desc, const void* q, const 
   a.keep_bits = dbg_keep_bits;
   a.scores = dbg_scores;
   return from_hip(sa::launch_skip_nm_softmax(a, (hipStream_t)stream));
+}
+
+sa_status sa_skip_softmax_decode_workspace(const sa_attn_desc* desc, float lambda,
+                                           int32_t num_splits, size_t* workspace_bytes,
+                                           int32_t* num_splits_used) {
+  if (desc == nullptr || workspace_bytes == nullptr) return SA_ERR_NULL;
+  if (desc->batch < 1 || desc->heads_q < 1 || desc->heads_kv < 1 || desc->seqlen_k < 1 ||
+      desc->head_dim < 1 || desc->heads_q % desc->heads_kv != 0)
+    return SA_ERR_SHAPE;
+  if (desc->head_dim != 64 && desc->head_dim != 128) return SA_ERR_UNSUPPORTED;
+  DecodePlan p;
+  const sa_status st = plan_decode(desc, lambda, num_splits, &p);
+  if (st != SA_OK) return st;
+  *workspace_bytes = p.bytes;
+  if (num_splits_used != nullptr) *num_splits_used = p.nsplit;
+  return SA_OK;
+}
+
+sa_status sa_skip_softmax_decode_fwd(const sa_attn_desc* desc, const void* q, const void* k,
+                                     const void* v, void* o, float lambda,
+                                     const int32_t* seqlens_k, int32_t num_splits,
+                                     void* workspace, size_t workspace_bytes,
+                                     uint8_t* tile_state, uint32_t* head_counters, float* lse,
+                                     float* dbg_tile_rowmax, void* stream) {
+  if (desc == nullptr) return SA_ERR_NULL;
+  // the query tile is the single query row: block_q plays no part
+  sa_attn_desc d = *desc;
+  d.block_q = 64;
+  sa_status st = check_attention(&d, q, k, v, o);
+  if (st != SA_OK) return st;
+  DecodePlan p;
+  st = plan_decode(&d, lambda, num_splits, &p);
+  if (st != SA_OK) return st;
+  if (workspace == nullptr) return SA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return SA_ERR_ALIGN;
+  if (workspace_bytes < p.bytes) return SA_ERR_SHAPE;
+  sa::DecodeArgs a{};
+  a.g = geometry(&d, q, k, v, o);
+  a.L32 = lambda == 0.f ? -INFINITY : (float)std::log2((double)lambda);
+  a.seqlens_k = seqlens_k;
+  a.block_k = d.block_k;
+  a.nKT = p.nKT;
+  a.nsplit = p.nsplit;
+  a.tiles_per_split = p.tps;
+  char* ws = static_cast<char*>(workspace);
+  a.scores = reinterpret_cast<float*>(ws + p.off_scores);
+  a.tmax = dbg_tile_rowmax != nullptr ? dbg_tile_rowmax : reinterpret_cast<float*>(ws + p.off_tmax);
+  a.part_m = reinterpret_cast<float*>(ws + p.off_pm);
+  a.part_l = reinterpret_cast<float*>(ws + p.off_pl);
+  a.part_o = reinterpret_cast<float*>(ws + p.off_po);
+  a.tile_state = tile_state;
+  a.counters = head_counters;
+  a.lse = lse;
+  return from_hip(sa::launch_skip_decode(a, (hipStream_t)stream));
 }
 
 sa_status sa_bitmask_route_prep(const sa_attn_desc* desc, const uint32_t* bitmask,

@@ -48,6 +48,25 @@ struct SkipNmArgs {
   float* scores;
 };
 
+// Decode-phase skip-softmax (one query token per head, key axis split over workgroups).
+constexpr int kMaxTilesPerSplit = 4096;
+
+struct DecodeArgs {
+  AttnGeom g;                           // Sq == 1, non-causal
+  float L32;
+  const int32_t* seqlens_k;             // optional [B], keys per sequence (clamped to [0, Sk])
+  int block_k;                          // 64 or 128: the decision tile
+  int nKT, nsplit, tiles_per_split;
+  float* scores;                        // workspace [B, Hkv, Sk, GM] raw q.k (GM >= G)
+  float* tmax;                          // [B, Hq, nKT] tile maxima, log2 domain
+  float* part_m;                        // [B, Hq, nsplit] split reference (max of kept maxima)
+  float* part_l;                        // [B, Hq, nsplit]
+  float* part_o;                        // [B, Hq, nsplit, D]
+  uint8_t* tile_state;                  // optional [B, Hq, nKT]
+  uint32_t* counters;                   // optional [B, Hq, 2]
+  float* lse;                           // optional [B, Hq]
+};
+
 struct RouteArgs {
   const uint32_t* bitmask;
   int32_t* n_exact;
@@ -86,6 +105,7 @@ struct ProxyArgs {
 hipError_t launch_skip_softmax(const SkipArgs& a, hipStream_t stream);
 hipError_t launch_nm_softmax(const NmArgs& a, hipStream_t stream);
 hipError_t launch_skip_nm_softmax(const SkipNmArgs& a, hipStream_t stream);
+hipError_t launch_skip_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_route_prep(const RouteArgs& a, hipStream_t stream);
 hipError_t launch_bsr_route_prep(const BsrRouteArgs& a, hipStream_t stream);
 hipError_t launch_proxy(const ProxyArgs& a, hipStream_t stream);

@@ -28,7 +28,8 @@ def test_exports_every_declared_symbol():
     names = declared_entry_points()
     assert {"sa_skip_softmax_fwd", "sa_nm_softmax_fwd", "sa_skip_nm_softmax_fwd",
             "sa_bitmask_route_prep", "sa_bsr_route_prep", "sa_skip_softmax_calibrate",
-            "sa_fit_threshold_calib",
+            "sa_fit_threshold_calib", "sa_skip_softmax_decode_workspace",
+            "sa_skip_softmax_decode_fwd",
             "sa_proxy_block_sparse_fwd", "sa_threshold_from_calib", "sa_status_str"} <= set(names)
     lib = ctypes.CDLL(sa.LIB_PATH)
     for n in names:
@@ -201,3 +202,51 @@ def test_skip_nm_rejects(lam, n, m, sink, recent, code):
     d64 = _desc(block_k=128)
     assert f(ctypes.byref(d64), FAKE, FAKE, FAKE, FAKE, 0.1, 2, 4, 0, 0, None, None, None, None,
              None, None, None) == sa.SA_ERR_UNSUPPORTED
+
+
+def _dec_desc(**kw):
+    base = dict(seqlen_q=1, seqlen_k=1024, heads_q=8, heads_kv=2, block_k=64,
+                q_stride=(8 * 128, 8 * 128, 128), o_stride=(8 * 128, 8 * 128, 128),
+                k_stride=(1024 * 2 * 128, 2 * 128, 128), v_stride=(1024 * 2 * 128, 2 * 128, 128))
+    base.update(kw)
+    return _desc(**base)
+
+
+def test_decode_workspace_plan():
+    nbytes, splits = ctypes.c_size_t(), ctypes.c_int32()
+    f = sa.raw.sa_skip_softmax_decode_workspace
+    d = _dec_desc()
+    assert f(ctypes.byref(d), ctypes.c_float(0.5), 0, ctypes.byref(nbytes), ctypes.byref(splits)) == sa.SA_OK
+    assert 1 <= splits.value <= 16 and nbytes.value % 256 == 0
+    # scores (B*Hkv*Sk*4 heads) + maxima + partials, each padded to 256 bytes
+    assert nbytes.value >= 1 * 2 * 1024 * 4 * 4 + 8 * 16 * 4
+    assert f(ctypes.byref(d), ctypes.c_float(0.5), 3, ctypes.byref(nbytes), ctypes.byref(splits)) == sa.SA_OK
+    assert splits.value == 3
+    # lambda > 1: one split, and an explicit larger count is refused
+    assert f(ctypes.byref(d), ctypes.c_float(2.0), 0, ctypes.byref(nbytes), ctypes.byref(splits)) == sa.SA_OK
+    assert splits.value == 1
+    assert f(ctypes.byref(d), ctypes.c_float(2.0), 4, ctypes.byref(nbytes), None) == sa.SA_ERR_UNSUPPORTED
+    assert f(ctypes.byref(_dec_desc(seqlen_q=2, causal=0)), ctypes.c_float(0.5), 0, ctypes.byref(nbytes), None) == sa.SA_ERR_UNSUPPORTED
+    assert f(ctypes.byref(_dec_desc(block_k=32)), ctypes.c_float(0.5), 0, ctypes.byref(nbytes), None) == sa.SA_ERR_UNSUPPORTED
+    assert f(ctypes.byref(_dec_desc(heads_q=64, heads_kv=2)), ctypes.c_float(0.5), 0, ctypes.byref(nbytes), None) == sa.SA_ERR_UNSUPPORTED
+    assert f(ctypes.byref(d), ctypes.c_float(-1.0), 0, ctypes.byref(nbytes), None) == sa.SA_ERR_VALUE
+    assert f(ctypes.byref(d), ctypes.c_float(0.5), -1, ctypes.byref(nbytes), None) == sa.SA_ERR_VALUE
+    assert f(None, ctypes.c_float(0.5), 0, ctypes.byref(nbytes), None) == sa.SA_ERR_NULL
+
+
+def test_decode_rejects():
+    d = _dec_desc()
+    f = sa.raw.sa_skip_softmax_decode_fwd
+
+    def call(desc=d, lam=0.5, ws=0x100000, ws_bytes=1 << 30, splits=0):
+        return f(ctypes.byref(desc) if desc is not None else None, FAKE, FAKE, FAKE, FAKE,
+                 ctypes.c_float(lam), None, splits, ws, ws_bytes, None, None, None, None, None)
+
+    assert call(desc=None) == sa.SA_ERR_NULL
+    assert call(ws=None) == sa.SA_ERR_NULL
+    assert call(ws=0x100010) == sa.SA_ERR_ALIGN          # not 256-byte aligned
+    assert call(ws_bytes=1024) == sa.SA_ERR_SHAPE
+    assert call(lam=float("nan")) == sa.SA_ERR_VALUE
+    assert call(lam=2.0, splits=2) == sa.SA_ERR_UNSUPPORTED
+    assert call(desc=_dec_desc(seqlen_q=4)) == sa.SA_ERR_UNSUPPORTED
+    assert call(desc=_dec_desc(causal=1, seqlen_k=1)) == sa.SA_ERR_UNSUPPORTED

@@ -38,6 +38,8 @@ CASES = [
     (1, 200, 200, 4, 2, 32, True, 64, 32),     # ragged tail, GQA, Br != Bc
     (2, 96, 160, 2, 1, 16, False, 32, 64),     # Sq != Sk non-causal, ragged K tile
     (1, 130, 130, 2, 2, 16, True, 128, 64),    # 2-row last Q tile
+    (2, 1, 300, 4, 2, 32, False, 1, 64),       # decode: one query row per head, ragged K tile
+    (1, 1, 640, 2, 2, 16, False, 1, 128),      # decode with 128-key tiles
 ]
 
 

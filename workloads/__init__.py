@@ -13,6 +13,9 @@ Generators (each a stand-in for a workload the pages describe but do not ship):
   with amplitude alpha = sqrt(sink_nats * sqrt(D)) added to every query and to the first
   ``n_sink`` keys, so each query's scaled logit on those keys is raised by ``sink_nats`` on
   average (attention sinks).  V iid N(0, 1).
+* ``gen_llm_decode`` -- one decode step on the LLM generator: K/V built as ``gen_llm`` builds
+  them, one query per head made like ``gen_llm``'s query at the sequence's last position, and
+  (optionally) ragged sequence lengths drawn uniformly from [S/2, S].
 * ``gen_video`` -- video-DiT-like: a 3-D (frame, row, col) token grid; Q = (E_q + Pos)/sqrt(2),
   K = (E_k + Pos)/sqrt(2) with Pos = sqrt(D) * W phi(t), phi a rank-64 random-Fourier embedding
   whose kernel is a separable Gaussian with the given sigmas (frames, rows, cols), W a D x 64
@@ -112,6 +115,44 @@ def gen_llm(seed, B, S, Hq, Hkv, D, rho=0.9, n_sink=4, sink_nats=3.0):
                 eq = _rng(seed, 12, b, hq).standard_normal((S, D))
                 q[b, :, hq] = to_bf16_bits((x + eq) / math.sqrt(2.0) + alpha * u)
     return q, k, v
+
+
+def gen_llm_decode(seed, B, S, Hq, Hkv, D, rho=0.9, n_sink=4, sink_nats=3.0, ragged=True):
+    """Decode-step inputs on the LLM generator: K/V [B,S,Hkv,D] as gen_llm builds them (latent
+    AR(1) keys with sink tokens) and one query per head, q [B,1,Hq,D], made like gen_llm's query at
+    the sequence's last position.  With ragged=True sequence b holds lens[b] keys, drawn uniformly
+    from [S/2, S] (the last sequence always holds S); otherwise every sequence holds S.  Returns
+    (q, k, v, lens int32 [B])."""
+    q = np.empty((B, 1, Hq, D), np.uint16)
+    k = np.empty((B, S, Hkv, D), np.uint16)
+    v = np.empty((B, S, Hkv, D), np.uint16)
+    G = Hq // Hkv
+    alpha = math.sqrt(sink_nats * math.sqrt(D))
+    lens = np.full(B, S, np.int32)
+    if ragged and B > 1:
+        lens[:-1] = _rng(seed, 14).integers(S // 2, S + 1, size=B - 1)
+
+    def one(bh):
+        b, hk = bh
+        last = int(lens[b]) - 1
+        rng = _rng(seed, 10, b, hk)
+        x = _ar1(rng.standard_normal((S, D)), rho)
+        u = rng.standard_normal(D)
+        u /= np.linalg.norm(u)
+        ek = rng.standard_normal((S, D))
+        kk = (x + ek) / math.sqrt(2.0)
+        kk[:n_sink] += alpha * u
+        k[b, :, hk] = to_bf16_bits(kk)
+        v[b, :, hk] = to_bf16_bits(_normal(_rng(seed, 11, b, hk), (S, D)))
+        for g in range(G):
+            hq = hk * G + g
+            eq = _rng(seed, 13, b, hq).standard_normal(D)
+            q[b, 0, hq] = to_bf16_bits((x[max(last, 0)] + eq) / math.sqrt(2.0) + alpha * u)
+
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(one, [(b, hk) for b in range(B) for hk in range(Hkv)]))
+    return q, k, v, lens
 
 
 def video_positions(frames, rows, cols):
@@ -239,7 +280,7 @@ THRESHOLD_TRIALS = [1e-4, 5e-4, 1e-3, 5e-3, 1e-2, 2e-2, 5e-2, 1e-1, 2e-1, 3e-1, 
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    path: str            # "skip", "nm" or "proxy"
+    path: str            # "skip", "nm", "proxy" or "decode"
     B: int
     Hq: int
     Hkv: int
@@ -269,6 +310,9 @@ class Workload:
             return gen_iid(self.seed, B, S, S, Hq, Hkv, self.D)
         if self.gen == "llm":
             return gen_llm(self.seed, B, S, Hq, Hkv, self.D)
+        if self.gen == "llm_decode":
+            return gen_llm_decode(self.seed, B, S, Hq, Hkv, self.D,
+                                  ragged=self.param("ragged", True))
         if self.gen == "video":
             grid = self.param("grid")
             if S != self.S:
@@ -287,6 +331,10 @@ WORKLOADS = {
                                      (("n", 2), ("m", 4), ("sink", 4), ("recent", 128))),
     "video_dit_s32760": Workload("video_dit_s32760", "skip", 1, 40, 40, 32760, 128, False, 128, 64,
                                  "video", 4, (("target_sparsity", 0.5), ("grid", (21, 30, 52)))),
+    "llm_decode_gqa_kv8192": Workload("llm_decode_gqa_kv8192", "decode", 16, 32, 8, 8192, 128,
+                                      False, 1, 64, "llm_decode", 6,
+                                      (("lambda", 1e-4), ("target_sparsity", 0.5),
+                                       ("ragged", True))),
     "proxy_bitmask_s16257": Workload("proxy_bitmask_s16257", "proxy", 1, 24, 24, 16257, 128, False,
                                      128, 128, "iid", 5, (("density", 0.25),)),
 }
