@@ -18,9 +18,11 @@
 // coalesced 16-byte loads (LPK = D/8 lanes per key row, 64/LPK rows per wave instruction):
 //   1 decode_scores   q.k for the G heads of a KV head (v_dot2 on packed bf16, LPK-lane sums),
 //                     written to a small fp32 workspace, and each tile's maximum;
-//   2 decode_attend   per split: the decisions (prefix max of earlier splits, then the running
-//                     max in order), then P.V over the kept tiles only, with P = 2^(t - r) for the
-//                     split's own reference r = max over its kept tiles (so no rescaling);
+//   2 decode_attend   per split: the decisions (for lambda <= 1 a wave-wide prefix-max scan over
+//                     64 tiles at a time, else the running max in order), then P.V over the kept
+//                     tiles only: per 64 keys one lane per key computes P = 2^(t - r) for the G
+//                     heads into LDS (r = the split's max over its kept tiles, so no rescaling),
+//                     and the key-row lanes accumulate P.V from it;
 //   3 decode_combine  the splits' (r, l, O) merged into O and the natural-log LSE.
 #include "kernels.h"
 #include "tile_core.h"
@@ -117,53 +119,196 @@ __global__ __launch_bounds__(kDecThreads) void decode_scores(DecodeArgs a) {
   const int kstride_b = (int)(g.ks[1] * 2);
   float* sc = a.scores + ((int64_t)u.b * g.Hkv + u.hk) * g.Sk * GM;
 
+  // Tiles past this sequence's keys are not visited.
   for (int t = u.t0 + wave; t < u.t1; t += kDecWaves) {
-    float* tm = a.tmax + ((int64_t)u.b * g.Hq + u.hk * G) * a.nKT + t;
-    if (t >= u.nvis) {   // beyond this sequence's keys: not visited
-      if (sub == 0 && c < G) tm[(int64_t)c * a.nKT] = -INFINITY;
-      continue;
-    }
-    float mx[GM];
+    if (t >= u.nvis && sub == 0 && c < G)
+      a.tmax[((int64_t)u.b * g.Hq + u.hk * G + c) * a.nKT + t] = -INFINITY;
+  }
+
+  // This wave's visited tiles t = t0 + wave + 4i as a stream of 64-key chunks; chunk q+1 is loaded
+  // while chunk q is reduced (two register buffers).
+  const int t_end = min(u.t1, u.nvis);
+  const int ntile = t_end > u.t0 + wave ? (t_end - (u.t0 + wave) + kDecWaves - 1) / kDecWaves : 0;
+  const int cpt = BC / 64;   // chunks per tile
+  const int nq = ntile * cpt;
+  auto chunk_key0 = [&](int q) { return (u.t0 + wave + kDecWaves * (q / cpt)) * BC + (q % cpt) * 64; };
+  auto load_chunk = [&](u32x4 (&kv)[kIt], int q) {
+    const int kbase = chunk_key0(q) + sub;
 #pragma unroll
-    for (int h = 0; h < GM; ++h) mx[h] = -INFINITY;
-    for (int k64 = 0; k64 < BC; k64 += 64) {
-      const int kbase = t * BC + k64 + sub;
-      u32x4 kv[kIt];
+    for (int it = 0; it < kIt; ++it)
+      kv[it] = load16(krs, (kbase + it * KPI) * kstride_b + c * 16);
+  };
+  float mx[GM];
 #pragma unroll
-      for (int it = 0; it < kIt; ++it)
-        kv[it] = load16(krs, (kbase + it * KPI) * kstride_b + c * 16);
+  for (int h = 0; h < GM; ++h) mx[h] = -INFINITY;
+  auto consume = [&](const u32x4 (&kv)[kIt], int q) {
+    const int kbase = chunk_key0(q) + sub;
 #pragma unroll
-      for (int it = 0; it < kIt; ++it) {
-        const int key = kbase + it * KPI;
-        float sv = -INFINITY;
+    for (int it = 0; it < kIt; ++it) {
+      const int key = kbase + it * KPI;
+      float sv = -INFINITY;
 #pragma unroll
-        for (int h = 0; h < GM; ++h) {
-          float s = row_sum<LPK>(dot8(qv[h], kv[it], 0.f));
-          s = key < u.len ? s : -INFINITY;
-          mx[h] = fmaxf(mx[h], s);
-          sv = c == h ? s : sv;
-        }
-        if (c < GM && key < g.Sk) sc[(int64_t)key * GM + c] = sv;
+      for (int h = 0; h < GM; ++h) {
+        float s = row_sum<LPK>(dot8(qv[h], kv[it], 0.f));
+        s = key < u.len ? s : -INFINITY;
+        mx[h] = fmaxf(mx[h], s);
+        sv = c == h ? s : sv;
       }
+      if (c < GM && key < g.Sk) sc[(int64_t)key * GM + c] = sv;
     }
-    // tile max over the key slots, in the log2 domain; lane (slot 0, chunk h) writes head h
-    float out = -INFINITY;
+    if (q % cpt == cpt - 1) {
+      // tile max over the key slots, in the log2 domain; lane (slot 0, chunk h) writes head h
+      const int t = u.t0 + wave + kDecWaves * (q / cpt);
+      float out = -INFINITY;
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      float m = mx[h];
-      for (int d = LPK; d < 64; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
-      out = c == h ? m * g.c32 : out;
+      for (int h = 0; h < GM; ++h) {
+        float m = mx[h];
+        for (int d = LPK; d < 64; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+        out = c == h ? m * g.c32 : out;
+        mx[h] = -INFINITY;
+      }
+      if (sub == 0 && c < G) a.tmax[((int64_t)u.b * g.Hq + u.hk * G + c) * a.nKT + t] = out;
     }
-    if (sub == 0 && c < G) tm[(int64_t)c * a.nKT] = out;
+  };
+  // The prefetches are unconditional (the index is clamped, so the tail re-reads the last chunk):
+  // a prefetch under a branch would make every later use wait for all loads in flight.
+  u32x4 kva[kIt], kvb[kIt];
+  if (nq > 0) {
+    load_chunk(kva, 0);
+    for (int q = 0; q < nq; q += 2) {
+      load_chunk(kvb, min(q + 1, nq - 1));
+      consume(kva, q);
+      load_chunk(kva, min(q + 2, nq - 1));
+      if (q + 1 < nq) consume(kvb, q + 1);
+    }
   }
 }
 
 // ---- 2: decisions and P.V over kept tiles ---------------------------------------------------------
+// Decisions (wave 0).  For lambda <= 1 the running max of the kept tiles before j is the prefix max
+// of all tile maxima before j, so the tiles of a split are decided 64 at a time with a wave-wide
+// prefix-max scan.  For lambda > 1 each head walks its tiles in order (maxima staged through LDS).
+// keepbits[j - t0] bit h: tile j kept by head h.
+template <int GM>
+__device__ __forceinline__ void decide_tiles(const DecodeArgs& a, const DecUnit& u, int lane,
+                                             const float (&pre)[kDecWaves][GM],
+                                             uint32_t* keepbits, float (&ref_s)[GM],
+                                             float (&stage)[GM][64]) {
+  const AttnGeom& g = a.g;
+  const int G = g.Hq / g.Hkv;
+  const float* tmax = a.tmax + ((int64_t)u.b * g.Hq + u.hk * G) * a.nKT;
+  const int64_t unit0 = (int64_t)u.b * g.Hq + u.hk * G;
+  float carry[GM], ref[GM];
+  unsigned vis_n[GM], skip_n[GM];
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    carry[h] = -INFINITY;
+    for (int w = 0; w < kDecWaves; ++w) carry[h] = fmaxf(carry[h], pre[w][h]);
+    ref[h] = -INFINITY;
+    vis_n[h] = skip_n[h] = 0u;
+  }
+  if (a.L32 <= 0.f) {
+    for (int j0 = u.t0; j0 < u.t1; j0 += 64) {
+      const int j = j0 + lane;
+      const bool in = j < u.t1, vis = in && j < u.nvis;
+      uint32_t bits = 0u;
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        if (h >= G) break;
+        const float M = vis ? tmax[(int64_t)h * a.nKT + j] : -INFINITY;
+        float incl = M;   // inclusive prefix max over the lanes
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const float up = __shfl_up(incl, d, 64);
+          if (lane >= d) incl = fmaxf(incl, up);
+        }
+        float excl = __shfl_up(incl, 1, 64);
+        excl = lane == 0 ? carry[h] : fmaxf(carry[h], excl);
+        const bool keep = vis && !(M < excl + a.L32);
+        bits |= (keep ? 1u : 0u) << h;
+        carry[h] = fmaxf(carry[h], __shfl(incl, 63, 64));
+        ref[h] = fmaxf(ref[h], keep ? M : -INFINITY);
+        vis_n[h] += __popcll(__ballot(vis));
+        skip_n[h] += __popcll(__ballot(vis && !keep));
+        if (in && a.tile_state != nullptr)
+          a.tile_state[(unit0 + h) * a.nKT + j] = vis ? (keep ? 0 : 1) : 2;
+      }
+      if (in) keepbits[j - u.t0] = bits;
+    }
+#pragma unroll
+    for (int h = 0; h < GM; ++h)
+      for (int d = 1; d < 64; d <<= 1) ref[h] = fmaxf(ref[h], __shfl_xor(ref[h], d, 64));
+  } else {
+    // lane h walks head h; the maxima of 64 tiles at a time come through LDS
+    const int h = lane;
+    float m = -INFINITY, rf = -INFINITY;
+    unsigned vn = 0u, sn = 0u;
+#pragma unroll
+    for (int hh = 0; hh < GM; ++hh)
+      if (h == hh) m = carry[hh];
+    for (int j0 = u.t0; j0 < u.t1; j0 += 64) {
+      const int j = j0 + lane;
+#pragma unroll
+      for (int hh = 0; hh < GM; ++hh)
+        stage[hh][lane] = (hh < G && j < u.nvis && j < u.t1) ? tmax[(int64_t)hh * a.nKT + j]
+                                                              : -INFINITY;
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the staged maxima are in LDS
+      __builtin_amdgcn_wave_barrier();
+      const int n = min(64, u.t1 - j0);
+      for (int jj = 0; jj < n; ++jj) {
+        const int jt = j0 + jj;
+        bool keep = false;
+        if (h < G && jt < u.nvis) {
+          const float M = stage[h][jj];
+          keep = !(M < m + a.L32);
+          if (keep) {
+            m = fmaxf(m, M);
+            rf = fmaxf(rf, M);
+          }
+          ++vn;
+          sn += keep ? 0u : 1u;
+          if (a.tile_state != nullptr) a.tile_state[(unit0 + h) * a.nKT + jt] = keep ? 0 : 1;
+        } else if (h < G && a.tile_state != nullptr) {
+          a.tile_state[(unit0 + h) * a.nKT + jt] = 2;
+        }
+        const uint64_t kb = __ballot(keep);
+        if (lane == 0) keepbits[jt - u.t0] = (uint32_t)kb;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int hh = 0; hh < GM; ++hh) {
+      ref[hh] = __shfl(rf, hh, 64);
+      vis_n[hh] = __shfl(vn, hh, 64);
+      skip_n[hh] = __shfl(sn, hh, 64);
+    }
+  }
+  if (lane < GM) {
+    float r = -INFINITY;
+#pragma unroll
+    for (int hh = 0; hh < GM; ++hh)
+      if (lane == hh) r = ref[hh];
+    ref_s[lane] = r;
+  }
+  if (lane < G && a.counters != nullptr) {
+    unsigned vn = 0u, sn = 0u;
+#pragma unroll
+    for (int hh = 0; hh < GM; ++hh)
+      if (lane == hh) {
+        vn = vis_n[hh];
+        sn = skip_n[hh];
+      }
+    atomicAdd(&a.counters[2 * (unit0 + lane)], vn);
+    atomicAdd(&a.counters[2 * (unit0 + lane) + 1], sn);
+  }
+}
+
 template <int D, int GM>
 __global__ __launch_bounds__(kDecThreads) void decode_attend(DecodeArgs a) {
   constexpr int LPK = D / 8;
   constexpr int KPI = 64 / LPK;
   constexpr int kIt = 64 / KPI;
+  constexpr int GQ = (GM + 3) / 4;   // 16-byte groups of P per key
   const AttnGeom& g = a.g;
   const DecUnit u = dec_unit(a);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -175,6 +320,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_attend(DecodeArgs a) {
   __shared__ float pre[kDecWaves][GM];
   __shared__ float ref_s[GM];
   __shared__ uint32_t keepbits[kMaxTilesPerSplit];
+  __shared__ float stage[GM][64];
+  __shared__ __attribute__((aligned(16))) float pbuf[kDecWaves][64][4 * GQ];
   __shared__ float red[kDecWaves][GM][D];
   __shared__ float lred[kDecWaves][GM];
 
@@ -188,39 +335,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attend(DecodeArgs a) {
     if (lane == 0) pre[wave][h] = m;
   }
   __syncthreads();
-
-  // decisions, in key order: lane h of wave 0 walks head h
-  if (wave == 0) {
-    const int h = lane;
-    float m = -INFINITY, ref = -INFINITY;
-    if (h < G)
-      for (int w = 0; w < kDecWaves; ++w) m = fmaxf(m, pre[w][h]);
-    unsigned visited = 0, skipped = 0;
-    const int64_t unit = (int64_t)u.b * g.Hq + u.hk * G + h;
-    for (int j = u.t0; j < u.t1; ++j) {
-      bool keep = false;
-      if (h < G && j < u.nvis) {
-        const float M = tmax[(int64_t)h * a.nKT + j];
-        keep = !(M < m + a.L32);
-        if (keep) {
-          m = fmaxf(m, M);
-          ref = fmaxf(ref, M);
-        }
-        ++visited;
-        skipped += keep ? 0u : 1u;
-        if (a.tile_state != nullptr) a.tile_state[unit * a.nKT + j] = keep ? 0 : 1;
-      } else if (h < G && a.tile_state != nullptr) {
-        a.tile_state[unit * a.nKT + j] = 2;
-      }
-      const uint64_t kb = __ballot(keep);
-      if (lane == 0) keepbits[j - u.t0] = (uint32_t)kb;
-    }
-    if (h < GM) ref_s[h] = ref;
-    if (h < G && a.counters != nullptr) {
-      atomicAdd(&a.counters[2 * unit], visited);
-      atomicAdd(&a.counters[2 * unit + 1], skipped);
-    }
-  }
+  if (wave == 0) decide_tiles<GM>(a, u, lane, pre, keepbits, ref_s, stage);
   __syncthreads();
 
   float ref[GM];
@@ -238,35 +353,87 @@ __global__ __launch_bounds__(kDecThreads) void decode_attend(DecodeArgs a) {
   const auto vrs = slab_rsrc(vslab, g.vs[1], u.len, D);
   const int vstride_b = (int)(g.vs[1] * 2);
   const float* sc = a.scores + ((int64_t)u.b * g.Hkv + u.hk) * g.Sk * GM;
+  float (*pw)[4 * GQ] = pbuf[wave];
 
-  for (int t = u.t0 + wave; t < u.t1; t += kDecWaves) {
-    const uint32_t kb = keepbits[t - u.t0];
-    if (kb == 0u) continue;   // skipped by every head: no V traffic
-    for (int k64 = 0; k64 < BC; k64 += 64) {
-      const int kbase = t * BC + k64 + sub;
-      u32x4 vv[kIt];
+  // This wave's kept tiles t = t0 + wave + 4i (some head keeps them) as a stream of 64-key chunks.
+  // The V rows and the scores of chunk n+1 are loaded while chunk n is reduced; the loads are
+  // unconditional (the last chunk is re-read at the end) so no use waits for the prefetch.
+  auto next_kept = [&](int t) {
+    while (t < u.t1 && keepbits[t - u.t0] == 0u) t += kDecWaves;
+    return t;
+  };
+  struct Chunk {
+    int t, k64;
+  };
+  auto advance = [&](Chunk q) {
+    if (q.k64 + 64 < BC) return Chunk{q.t, q.k64 + 64};
+    return Chunk{next_kept(q.t + kDecWaves), 0};
+  };
+  auto load_chunk = [&](u32x4 (&vv)[kIt], float (&sv)[GM], Chunk q) {
+    const int kbase = q.t * BC + q.k64 + sub;
 #pragma unroll
-      for (int it = 0; it < kIt; ++it)
-        vv[it] = load16(vrs, (kbase + it * KPI) * vstride_b + c * 16);
+    for (int it = 0; it < kIt; ++it)
+      vv[it] = load16(vrs, (kbase + it * KPI) * vstride_b + c * 16);
+    const int key = q.t * BC + q.k64 + lane;   // one key per lane for P
+    const float* sp = sc + (int64_t)min(key, g.Sk - 1) * GM;
 #pragma unroll
-      for (int it = 0; it < kIt; ++it) {
-        const int key = kbase + it * KPI;
-        if (key >= u.len) break;   // the rest of this tile is past the sequence
-        const float* sk = sc + (int64_t)key * GM;
-        float vf[8];
+    for (int h = 0; h < GM; ++h) sv[h] = sp[h];
+  };
+  auto reduce_chunk = [&](const u32x4 (&vv)[kIt], const float (&sv)[GM], Chunk q) {
+    const uint32_t kb = keepbits[q.t - u.t0];
+    // P of the 64 keys, one key per lane, into this wave's LDS slot; l from the same values
+    const bool valid = q.t * BC + q.k64 + lane < u.len;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          vf[2 * i] = bf16_lo(vv[it][i]);
-          vf[2 * i + 1] = bf16_hi(vv[it][i]);
-        }
+    for (int h = 0; h < 4 * GQ; ++h) {
+      float p = 0.f;
+      if (h < GM && ((kb >> h) & 1u) && valid)
+        p = __builtin_amdgcn_exp2f(sv[h < GM ? h : 0] * g.c32 - ref[h < GM ? h : 0]);
+      if (h < GM) ls[h] += p;
+      pw[lane][h] = p;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): P is in LDS for the whole wave
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int h = 0; h < GM; ++h) {
-          const float p = ((kb >> h) & 1u) ? __builtin_amdgcn_exp2f(sk[h] * g.c32 - ref[h]) : 0.f;
-          ls[h] += c == 0 ? p : 0.f;
+    for (int it = 0; it < kIt; ++it) {
+      const int kl = sub + it * KPI;   // key within the 64
+      float vf[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] += p * vf[e];
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = vv[it][i];
+        vf[2 * i] = bf16_lo(w);
+        vf[2 * i + 1] = bf16_hi(w);
+      }
+#pragma unroll
+      for (int q4 = 0; q4 < GQ; ++q4) {
+        const f32x4 p4 = *(const f32x4*)&pw[kl][4 * q4];
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+          const int h = 4 * q4 + hh;
+          if (h >= GM) break;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] += p4[hh] * vf[e];
         }
       }
+    }
+    __builtin_amdgcn_wave_barrier();   // every lane has read P before the next chunk rewrites it
+  };
+
+  Chunk cur{next_kept(u.t0 + wave), 0};
+  if (cur.t < u.t1) {
+    u32x4 vva[kIt], vvb[kIt];
+    float sva[GM], svb[GM];
+    load_chunk(vva, sva, cur);
+    while (true) {
+      Chunk nxt = advance(cur);
+      load_chunk(vvb, svb, nxt.t < u.t1 ? nxt : cur);
+      reduce_chunk(vva, sva, cur);
+      if (nxt.t >= u.t1) break;
+      cur = nxt;
+      nxt = advance(cur);
+      load_chunk(vva, sva, nxt.t < u.t1 ? nxt : cur);
+      reduce_chunk(vvb, svb, cur);
+      if (nxt.t >= u.t1) break;
+      cur = nxt;
     }
   }
 
