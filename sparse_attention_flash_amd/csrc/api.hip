@@ -111,8 +111,9 @@ sa_status plan_decode(const sa_attn_desc* d, float lambda, int32_t num_splits, D
   } else if (num_splits > 0) {
     ns = num_splits;
   } else {
-    // about four workgroups per compute unit
-    ns = (int)std::min<int64_t>(std::max<int64_t>(1, (1024 + units - 1) / units), p->nKT);
+    // about one workgroup per compute unit: a longer key range per wave hides the start-up of
+    // its load stream better than more, shorter workgroups do
+    ns = (int)std::min<int64_t>(std::max<int64_t>(1, (256 + units - 1) / units), p->nKT);
   }
   ns = std::min(ns, p->nKT);
   int tps = (p->nKT + ns - 1) / ns;
@@ -127,7 +128,7 @@ sa_status plan_decode(const sa_attn_desc* d, float lambda, int32_t num_splits, D
   const size_t heads = (size_t)d->batch * d->heads_q;
   size_t off = 0;
   p->off_scores = off;
-  off += up((size_t)units * d->seqlen_k * p->GM * sizeof(float));
+  off += up((size_t)units * p->GM * p->nKT * d->block_k * sizeof(float));
   p->off_tmax = off;
   off += up(heads * p->nKT * sizeof(float));
   p->off_pm = off;

@@ -14,10 +14,10 @@
 // starts from the max of the earlier splits' tile maxima.  (lambda > 1 runs as one split.)
 //
 // Decode reads every K row once and each kept V row once for G query heads: about 4 flops per
-// byte, far below what MFMA needs, so the three kernels are VALU code that streams K/V with
-// coalesced 16-byte loads (LPK = D/8 lanes per key row, 64/LPK rows per wave instruction):
-//   1 decode_scores   q.k for the G heads of a KV head (v_dot2 on packed bf16, LPK-lane sums),
-//                     written to a small fp32 workspace, and each tile's maximum;
+// byte, so the kernels are bound by the K/V stream.  K and V are read straight into registers
+// with 16-byte loads, and each 64-key chunk's loads are in flight while the previous chunk is used:
+//   1 decode_scores   q.k for the G heads of a KV head on MFMA (the heads as the columns of
+//                     S^T = K.Q^T), written to a small fp32 workspace, and each tile's maximum;
 //   2 decode_attend   per split: the decisions (for lambda <= 1 a wave-wide prefix-max scan over
 //                     64 tiles at a time, else the running max in order), then P.V over the kept
 //                     tiles only: per 64 keys one lane per key computes P = 2^(t - r) for the G
@@ -32,38 +32,6 @@ namespace {
 
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-template <int Ctrl>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), Ctrl, 0xF, 0xF, true));
-}
-
-// Sum over the LPK (16 or 8) lanes of one key row, with identical bits in every lane: xor-1 and
-// xor-2 swaps within quads, the 8-lane half mirror, then the 16-lane mirror (each step adds two
-// equal-by-construction halves in both orders, and fp32 addition commutes).
-template <int LPK>
-__device__ __forceinline__ float row_sum(float x) {
-  x += dpp_f<0xB1>(x);    // quad_perm [1,0,3,2]
-  x += dpp_f<0x4E>(x);    // quad_perm [2,3,0,1]
-  x += dpp_f<0x141>(x);   // row_half_mirror
-  if constexpr (LPK == 16) x += dpp_f<0x140>(x);   // row_mirror
-  return x;
-}
-
-// Each word is copied out of the vector before the bit cast: a __builtin_bit_cast applied to a
-// vector element expression itself compiles to a read of element 0.
-__device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b, float acc) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t x = a[i], y = b[i];
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x),
-                                          __builtin_bit_cast(bf16x2_t, y), acc, false);
-  }
-  return acc;
-}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -90,89 +58,111 @@ __device__ __forceinline__ DecUnit dec_unit(const DecodeArgs& a) {
 }
 
 // ---- 1: scores and tile maxima --------------------------------------------------------------------
+// S^T = K.Q^T on v_mfma_f32_32x32x16_bf16, one 32-key block at a time: A = 32 K rows (lane l: key
+// l%32, the 8 values at d = 16ks + 8(l/32)), B = Q^T with the G heads as columns (columns past G
+// are zero).  Only G of the 32 columns do useful work, but the matrix cores still need about an
+// eighth of the issue cycles of the same dot products on the VALU, so the kernel stays bound by
+// the K stream.  Lane l then holds, for head l%32, keys 8i + 4(l/32) + {0..3} in elements
+// 4i..4i+3.  Scores go to the workspace head-major, [GM][nKT*block_k] per (batch, KV head).
 template <int D, int GM>
 __global__ __launch_bounds__(kDecThreads) void decode_scores(DecodeArgs a) {
-  constexpr int LPK = D / 8;         // lanes per key row (16 B each)
-  constexpr int KPI = 64 / LPK;      // key rows per wave instruction
-  constexpr int kIt = 64 / KPI;      // instructions per 64 keys
-  static_assert(GM <= LPK, "one writer lane per head");
+  constexpr int KS = D / 16;   // MFMA k-steps per key block
   const AttnGeom& g = a.g;
   const DecUnit u = dec_unit(a);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int sub = lane / LPK, c = lane % LPK;
+  const int col = lane & 31, hl = lane >> 5;
   const int G = g.Hq / g.Hkv;
   const int BC = a.block_k;
+  const int64_t row_len = (int64_t)a.nKT * BC;   // scores row stride (a multiple of 64 keys)
 
-  // q of the G heads: 8 values of chunk c each (zeros for padding heads h >= G)
-  u32x4 qv[GM];
+  bf16x8 qf[KS];
+  {
+    const __bf16* qp = (const __bf16*)g.q + u.b * g.qs[0] + (u.hk * G + min(col, G - 1)) * g.qs[2];
 #pragma unroll
-  for (int h = 0; h < GM; ++h) {
-    qv[h] = u32x4{0u, 0u, 0u, 0u};
-    if (h < G) {
-      const __bf16* qp = (const __bf16*)g.q + u.b * g.qs[0] + (u.hk * G + h) * g.qs[2];
-      qv[h] = *(const u32x4*)(qp + 8 * c);
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 x = *(const bf16x8*)(qp + 16 * ks + 8 * hl);
+      if (col >= G) x = bf16x8{};
+      qf[ks] = x;
     }
   }
   const __bf16* kslab = (const __bf16*)g.k + u.b * g.ks[0] + u.hk * g.ks[2];
   const auto krs = slab_rsrc(kslab, g.ks[1], u.len, D);
   const int kstride_b = (int)(g.ks[1] * 2);
-  float* sc = a.scores + ((int64_t)u.b * g.Hkv + u.hk) * g.Sk * GM;
+  float* sc = a.scores + ((int64_t)u.b * g.Hkv + u.hk) * GM * row_len;
+  // A chunk's scores go through LDS so that the whole wave stores them with full 16-byte lanes
+  // (the lanes holding them are only 2*GM of 64).
+  __shared__ __attribute__((aligned(16))) float sbuf[kDecWaves][GM][64];
+  float (*sw)[64] = sbuf[wave];
 
   // Tiles past this sequence's keys are not visited.
   for (int t = u.t0 + wave; t < u.t1; t += kDecWaves) {
-    if (t >= u.nvis && sub == 0 && c < G)
-      a.tmax[((int64_t)u.b * g.Hq + u.hk * G + c) * a.nKT + t] = -INFINITY;
+    if (t >= u.nvis && lane < G)
+      a.tmax[((int64_t)u.b * g.Hq + u.hk * G + lane) * a.nKT + t] = -INFINITY;
   }
 
   // This wave's visited tiles t = t0 + wave + 4i as a stream of 64-key chunks; chunk q+1 is loaded
-  // while chunk q is reduced (two register buffers).
+  // while chunk q is multiplied (two register buffers).  The prefetches are unconditional (the
+  // index is clamped, so the tail re-reads the last chunk): a prefetch under a branch would make
+  // every later use wait for all loads in flight.
   const int t_end = min(u.t1, u.nvis);
   const int ntile = t_end > u.t0 + wave ? (t_end - (u.t0 + wave) + kDecWaves - 1) / kDecWaves : 0;
   const int cpt = BC / 64;   // chunks per tile
   const int nq = ntile * cpt;
   auto chunk_key0 = [&](int q) { return (u.t0 + wave + kDecWaves * (q / cpt)) * BC + (q % cpt) * 64; };
-  auto load_chunk = [&](u32x4 (&kv)[kIt], int q) {
-    const int kbase = chunk_key0(q) + sub;
+  auto load_chunk = [&](bf16x8 (&kv)[2][KS], int q) {
+    const int key0 = chunk_key0(q);
 #pragma unroll
-    for (int it = 0; it < kIt; ++it)
-      kv[it] = load16(krs, (kbase + it * KPI) * kstride_b + c * 16);
-  };
-  float mx[GM];
+    for (int kb = 0; kb < 2; ++kb) {
+      const int off = (key0 + 32 * kb + col) * kstride_b + 16 * hl;
 #pragma unroll
-  for (int h = 0; h < GM; ++h) mx[h] = -INFINITY;
-  auto consume = [&](const u32x4 (&kv)[kIt], int q) {
-    const int kbase = chunk_key0(q) + sub;
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int key = kbase + it * KPI;
-      float sv = -INFINITY;
-#pragma unroll
-      for (int h = 0; h < GM; ++h) {
-        float s = row_sum<LPK>(dot8(qv[h], kv[it], 0.f));
-        s = key < u.len ? s : -INFINITY;
-        mx[h] = fmaxf(mx[h], s);
-        sv = c == h ? s : sv;
-      }
-      if (c < GM && key < g.Sk) sc[(int64_t)key * GM + c] = sv;
+      for (int ks = 0; ks < KS; ++ks)
+        kv[kb][ks] = __builtin_bit_cast(bf16x8, load16(krs, off + 32 * ks));
     }
+  };
+  float mx = -INFINITY;   // running max of this lane's keys in the current tile (its head)
+  auto consume = [&](const bf16x8 (&kv)[2][KS], int q) {
+    const int key0 = chunk_key0(q);
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(kv[kb][ks], qf[ks], s[kb]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      // keys past the sequence: -inf (their rows read as zeros)
+      mask_block(s[kb], kb, u.len - key0 - 4 * hl);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      if (col < GM) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          *(f32x4*)&sw[col][32 * kb + 8 * i4 + 4 * hl] =
+              f32x4{s[kb][4 * i4], s[kb][4 * i4 + 1], s[kb][4 * i4 + 2], s[kb][4 * i4 + 3]};
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the chunk's scores are in LDS
+    __builtin_amdgcn_wave_barrier();
+    // GM rows of 64 keys = GM*16 lanes of 16 bytes
+#pragma unroll
+    for (int r = 0; r < (GM * 16 + 63) / 64; ++r) {
+      const int e = 64 * r + lane;
+      if (e < GM * 16) {
+        const int hh = e >> 4, k4 = (e & 15) * 4;
+        *(f32x4*)(sc + hh * row_len + key0 + k4) = *(const f32x4*)&sw[hh][k4];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();   // read before the next chunk rewrites the buffer
     if (q % cpt == cpt - 1) {
-      // tile max over the key slots, in the log2 domain; lane (slot 0, chunk h) writes head h
+      // tile max of head col over both lane halves, in the log2 domain
       const int t = u.t0 + wave + kDecWaves * (q / cpt);
-      float out = -INFINITY;
-#pragma unroll
-      for (int h = 0; h < GM; ++h) {
-        float m = mx[h];
-        for (int d = LPK; d < 64; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
-        out = c == h ? m * g.c32 : out;
-        mx[h] = -INFINITY;
-      }
-      if (sub == 0 && c < G) a.tmax[((int64_t)u.b * g.Hq + u.hk * G + c) * a.nKT + t] = out;
+      const float m = half_max(mx);
+      if (hl == 0 && col < G)
+        a.tmax[((int64_t)u.b * g.Hq + u.hk * G + col) * a.nKT + t] = m * g.c32;
+      mx = -INFINITY;
     }
   };
-  // The prefetches are unconditional (the index is clamped, so the tail re-reads the last chunk):
-  // a prefetch under a branch would make every later use wait for all loads in flight.
-  u32x4 kva[kIt], kvb[kIt];
+  bf16x8 kva[2][KS], kvb[2][KS];
   if (nq > 0) {
     load_chunk(kva, 0);
     for (int q = 0; q < nq; q += 2) {
@@ -322,6 +312,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attend(DecodeArgs a) {
   __shared__ uint32_t keepbits[kMaxTilesPerSplit];
   __shared__ float stage[GM][64];
   __shared__ __attribute__((aligned(16))) float pbuf[kDecWaves][64][4 * GQ];
+  __shared__ uint16_t klist[kDecWaves][kMaxTilesPerSplit / kDecWaves];
   __shared__ float red[kDecWaves][GM][D];
   __shared__ float lred[kDecWaves][GM];
 
@@ -352,37 +343,40 @@ __global__ __launch_bounds__(kDecThreads) void decode_attend(DecodeArgs a) {
   const __bf16* vslab = (const __bf16*)g.v + u.b * g.vs[0] + u.hk * g.vs[2];
   const auto vrs = slab_rsrc(vslab, g.vs[1], u.len, D);
   const int vstride_b = (int)(g.vs[1] * 2);
-  const float* sc = a.scores + ((int64_t)u.b * g.Hkv + u.hk) * g.Sk * GM;
+  const int64_t row_len = (int64_t)a.nKT * BC;   // scores row stride
+  const float* sc = a.scores + ((int64_t)u.b * g.Hkv + u.hk) * GM * row_len;
   float (*pw)[4 * GQ] = pbuf[wave];
 
-  // This wave's kept tiles t = t0 + wave + 4i (some head keeps them) as a stream of 64-key chunks.
-  // The V rows and the scores of chunk n+1 are loaded while chunk n is reduced; the loads are
-  // unconditional (the last chunk is re-read at the end) so no use waits for the prefetch.
-  auto next_kept = [&](int t) {
-    while (t < u.t1 && keepbits[t - u.t0] == 0u) t += kDecWaves;
-    return t;
-  };
-  struct Chunk {
-    int t, k64;
-  };
-  auto advance = [&](Chunk q) {
-    if (q.k64 + 64 < BC) return Chunk{q.t, q.k64 + 64};
-    return Chunk{next_kept(q.t + kDecWaves), 0};
-  };
-  auto load_chunk = [&](u32x4 (&vv)[kIt], float (&sv)[GM], Chunk q) {
-    const int kbase = q.t * BC + q.k64 + sub;
+  // This wave's kept tiles t = t0 + wave + 4i (kept by some head) listed in LDS, then walked as
+  // 64-key chunks; the V rows and scores of chunk q+1 are loaded while chunk q is reduced.  The
+  // prefetches are unconditional (clamped index), so the compiler's waits leave them in flight.
+  uint16_t* list = klist[wave];
+  int nkept = 0;
+  for (int i0 = 0; u.t0 + wave + kDecWaves * i0 < u.t1; i0 += 64) {
+    const int t = u.t0 + wave + kDecWaves * (i0 + lane);
+    const bool kept = t < u.t1 && keepbits[t - u.t0] != 0u;
+    const uint64_t m = __ballot(kept);
+    if (kept) list[nkept + __popcll(m & ((1ull << lane) - 1ull))] = (uint16_t)(t - u.t0);
+    nkept += __popcll(m);
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the list is in LDS for the whole wave
+  __builtin_amdgcn_wave_barrier();
+  const int cpt = BC / 64;
+  const int nq = nkept * cpt;
+  auto chunk_key0 = [&](int q) { return (u.t0 + list[q / cpt]) * BC + (q % cpt) * 64; };
+  auto load_chunk = [&](u32x4 (&vv)[kIt], float (&sv)[GM], int q) {
+    const int key0 = chunk_key0(q);
 #pragma unroll
     for (int it = 0; it < kIt; ++it)
-      vv[it] = load16(vrs, (kbase + it * KPI) * vstride_b + c * 16);
-    const int key = q.t * BC + q.k64 + lane;   // one key per lane for P
-    const float* sp = sc + (int64_t)min(key, g.Sk - 1) * GM;
+      vv[it] = load16(vrs, (key0 + sub + it * KPI) * vstride_b + c * 16);
 #pragma unroll
-    for (int h = 0; h < GM; ++h) sv[h] = sp[h];
+    for (int h = 0; h < GM; ++h) sv[h] = sc[h * row_len + key0 + lane];   // one key per lane
   };
-  auto reduce_chunk = [&](const u32x4 (&vv)[kIt], const float (&sv)[GM], Chunk q) {
-    const uint32_t kb = keepbits[q.t - u.t0];
+  auto reduce_chunk = [&](const u32x4 (&vv)[kIt], const float (&sv)[GM], int q) {
+    const int key0 = chunk_key0(q);
+    const uint32_t kb = keepbits[key0 / BC - u.t0];
     // P of the 64 keys, one key per lane, into this wave's LDS slot; l from the same values
-    const bool valid = q.t * BC + q.k64 + lane < u.len;
+    const bool valid = key0 + lane < u.len;
 #pragma unroll
     for (int h = 0; h < 4 * GQ; ++h) {
       float p = 0.f;
@@ -417,23 +411,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_attend(DecodeArgs a) {
     }
     __builtin_amdgcn_wave_barrier();   // every lane has read P before the next chunk rewrites it
   };
-
-  Chunk cur{next_kept(u.t0 + wave), 0};
-  if (cur.t < u.t1) {
+  if (nq > 0) {
     u32x4 vva[kIt], vvb[kIt];
     float sva[GM], svb[GM];
-    load_chunk(vva, sva, cur);
-    while (true) {
-      Chunk nxt = advance(cur);
-      load_chunk(vvb, svb, nxt.t < u.t1 ? nxt : cur);
-      reduce_chunk(vva, sva, cur);
-      if (nxt.t >= u.t1) break;
-      cur = nxt;
-      nxt = advance(cur);
-      load_chunk(vva, sva, nxt.t < u.t1 ? nxt : cur);
-      reduce_chunk(vvb, svb, cur);
-      if (nxt.t >= u.t1) break;
-      cur = nxt;
+    load_chunk(vva, sva, 0);
+    for (int q = 0; q < nq; q += 2) {
+      load_chunk(vvb, svb, min(q + 1, nq - 1));
+      reduce_chunk(vva, sva, q);
+      load_chunk(vva, sva, min(q + 2, nq - 1));
+      if (q + 1 < nq) reduce_chunk(vvb, svb, q + 1);
     }
   }
 

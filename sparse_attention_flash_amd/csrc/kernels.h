@@ -57,7 +57,7 @@ struct DecodeArgs {
   const int32_t* seqlens_k;             // optional [B], keys per sequence (clamped to [0, Sk])
   int block_k;                          // 64 or 128: the decision tile
   int nKT, nsplit, tiles_per_split;
-  float* scores;                        // workspace [B, Hkv, Sk, GM] raw q.k (GM >= G)
+  float* scores;                        // workspace [B, Hkv, GM, nKT*block_k] raw q.k (GM >= G)
   float* tmax;                          // [B, Hq, nKT] tile maxima, log2 domain
   float* part_m;                        // [B, Hq, nsplit] split reference (max of kept maxima)
   float* part_l;                        // [B, Hq, nsplit]
