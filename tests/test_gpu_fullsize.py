@@ -171,6 +171,74 @@ def test_nm_softmax_full_size(n, m):
     assert err(lse_got[valid], lse_ref[valid])[0] < 2e-3
 
 
+def test_skip_nm_full_size():
+    """Skip-softmax with 2:4 inside kept tiles on the N:M workload at the threshold bench.py times
+    (target 0.5 lowered through the pages' model)."""
+    wl = W.WORKLOADS["llm_prefill_nm_s4096"]
+    announce("skip + 2:4 full size")
+    q, k, v = wl.generate()
+    B, Sq, Hq, D = q.shape
+    Sk = k.shape[1]
+    Br, Bc = wl.block_q, wl.block_k
+    nQT, nKT, Wd = -(-Sq // Br), -(-Sk // Bc), -(-Sk // 32)
+    sink, recent = wl.param("sink"), wl.param("recent")
+    _, lam, _ = sa.sa_threshold_from_calib(W.CALIB_A, W.CALIB_B, 0.5, Sk)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o = torch.empty_like(qd)
+    st = torch.full((B, Hq, nQT, nKT), 255, dtype=torch.uint8, device="cuda")
+    cnt = torch.zeros((B, Hq, 2), dtype=torch.int32, device="cuda")
+    lse = torch.empty((B, Hq, Sq), device="cuda")
+    rm = torch.empty((B * Hq * nQT, nKT, Br), device="cuda")
+    bits = torch.empty((B, Hq, Sq, Wd), dtype=torch.int32, device="cuda")
+    sc = torch.empty((B, Hq, Sq, Sk), device="cuda")
+    sa.sa_skip_nm_softmax_fwd(qd, kd, vd, o, lam, 2, 4, sink, recent, causal=True, block_q=Br,
+                              block_k=Bc, tile_state=st, head_counters=cnt, lse=lse,
+                              dbg_tile_rowmax=rm, dbg_keep_bits=bits, dbg_scores=sc)
+    torch.cuda.synchronize()
+    state = st.cpu().numpy()
+    counts = cnt.cpu().numpy()
+    assert (counts[..., 0] == (state != 2).sum((-1, -2))).all()
+    assert (counts[..., 1] == (state == 1).sum((-1, -2))).all()
+    assert 0 < (state == 1).sum() < (state != 2).sum()
+
+    units = sample_units(B * Hq * nQT, wl.seed + 77)
+    ud = torch.from_numpy(units).to("cuda")
+    rowmax_in = np.zeros((B * Hq * nQT, nKT, Br), np.float32)
+    rowmax_in[units] = rm[ud].cpu().numpy()
+    rows = []
+    for u in units:
+        bh, qt = divmod(int(u), nQT)
+        b, h = divmod(bh, Hq)
+        rows += [(b, h, r) for r in range(qt * Br, min(Sq, qt * Br + Br))]
+    rows = np.array(rows)
+    ri = torch.from_numpy(rows).to("cuda")
+    scores_in = np.zeros((B, Hq, Sq, Sk), np.float32)
+    scores_in[rows[:, 0], rows[:, 1], rows[:, 2]] = sc[ri[:, 0], ri[:, 1], ri[:, 2]].cpu().numpy()
+    keep_all = bits.cpu().numpy().view(np.uint32)
+    kw = dict(causal=True, block_q=Br, block_k=Bc, scale=wl.scale, lam=lam, n=2, m=4, sink=sink,
+              recent=recent, units=units)
+    flat = state.reshape(-1, nKT)[units]
+    valid = row_valid(units, Hq, nQT, Br, Sq)
+    gpu_bits = np.zeros((units.size, Br, Wd), np.uint32)
+    for i, u in enumerate(units):
+        bh, qt = divmod(int(u), nQT)
+        b, h = divmod(bh, Hq)
+        r0, r1 = qt * Br, min(Sq, qt * Br + Br)
+        gpu_bits[i, : r1 - r0] = keep_all[b, h, r0:r1]
+
+    _, _, st_r, _, kb_r = oracle.skip_nm_softmax(q, k, v, mode=1, rowmax_in=rowmax_in,
+                                                 scores_in=scores_in, **kw)
+    assert np.array_equal(st_r, flat), "replayed tile states differ"
+    assert np.array_equal(kb_r[valid], gpu_bits[valid]), "replayed keep bits differ"
+    _, _, st_i, _, _ = oracle.skip_nm_softmax(q, k, v, mode=0, **kw)
+    vis = flat != 2
+    assert (st_i[vis] == flat[vis]).mean() >= 0.999
+    o_ref, lse_ref, _, _, _ = oracle.skip_nm_softmax(q, k, v, mode=2, state_in=state,
+                                                     keep_in=keep_all, **kw)
+    got = o_rows(from_dev_bf16(o), units, Hq, nQT, Br, Sq)
+    assert_output_parity(got[valid], o_ref[valid], "skip + 2:4 O")
+
+
 def test_proxy_full_size():
     wl = W.WORKLOADS["proxy_bitmask_s16257"]
     announce("proxy full size")
