@@ -121,14 +121,13 @@ __device__ __forceinline__ void tile_row_max(const f32x16 (&s)[2][QB], float c32
 template <int QB>
 struct TileState {
   float M[QB];
-  uint32_t kbits[QB];
   bool keep;
 };
 
 // Softmax of a kept tile fused with its P.V product.  For each 16-key chunk: exponentials of the
 // chunk (VALU), then the MFMAs that consume them, so the VALU work of one chunk overlaps the MFMAs
-// of the previous one.  keep bits (N:M) zero dropped keys; Pol::weight (proxy) scales each key's
-// row-sum term.  The row sum adds the fp32 weights (before their rounding to bf16 for P.V), which
+// of the previous one.  Keys a filter dropped (N:M) arrive as -inf and get weight 0;
+// Pol::weight (proxy) scales each key's row-sum term.  The row sum adds the fp32 weights (before their rounding to bf16 for P.V), which
 // keeps the LSE at fp32 accuracy.
 template <int D, int QB, class Pol>
 __device__ __forceinline__ void softmax_pv(const Pol& pol, int step, const f32x16 (&s)[2][QB],
@@ -181,7 +180,6 @@ __device__ __forceinline__ void softmax_pv(const Pol& pol, int step, const f32x1
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * c + e;
         float p = __builtin_amdgcn_exp2f(s[kb][qb][r] * c32 - muse[qb]);
-        if constexpr (Pol::kFilter) p = ((ts.kbits[qb] >> (kb * 16 + r)) & 1u) ? p : 0.f;
         if constexpr (Pol::kWeighted) {
           rs += weighted ? p * pol.weight(step, kb, r, lane) : p;
         } else {
@@ -226,7 +224,7 @@ __device__ __forceinline__ void softmax_pv(const Pol& pol, int step, const f32x1
 //   void mask(int step, f32x16 (&s)[2][QB], int lane) const;        -inf for masked keys
 //   static constexpr bool kDecide, kFilter, kWeighted;
 //   bool negligible(const float (&M)[QB], const float (&mt)[QB], int lane) const;   [kDecide]
-//   void filter(int step, const f32x16 (&s)[2][QB], uint32_t (&bits)[QB], int lane) const; [kFilter]
+//   void filter(int step, f32x16 (&s)[2][QB], int lane) const;  dropped keys -> -inf   [kFilter]
 //   bool weighted(int step) const; float weight(int step, int kb, int r, int lane) const; [kWeighted]
 //   void record(int step, bool keep, const float (&M)[QB], int wave, int lane, bool leader);
 // On return o, mref and l hold the unnormalised accumulator, exponent reference and row-sum
@@ -260,14 +258,13 @@ struct Mainloop {
     DmaV::copy(sm.v[step & 1], t.v, t.v_bytes, t.v_stride_b, vlo, wave);
   }
 
-  // S(step) from the K tile in LDS, masked, with its row maxima and N:M bits.
+  // S(step) from the K tile in LDS, masked, with its row maxima; a filtering policy (N:M) then
+  // sets the scores of the keys it drops to -inf.
   __device__ __forceinline__ void scores(int step, f32x16 (&s)[2][QB], TS& ts) {
     qk_tile<D, QB>(sm.k[step & 1], qf, s, lane);
     pol.mask(step, s, lane);
     tile_row_max<QB>(s, c32, ts.M);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) ts.kbits[qb] = ~0u;
-    if constexpr (Pol::kFilter) pol.filter(step, s, ts.kbits, lane);
+    if constexpr (Pol::kFilter) pol.filter(step, s, lane);
   }
 
   // Each wave publishes "some row of this tile is not negligible" in LDS; the votes are read

@@ -106,7 +106,7 @@ struct KeyTiles {
   __device__ __forceinline__ bool negligible(const float (&)[QB], const float (&)[QB], int) const {
     return false;
   }
-  __device__ __forceinline__ void filter(int, const f32x16 (&)[2][QB], uint32_t (&)[QB], int) const {}
+  __device__ __forceinline__ void filter(int, f32x16 (&)[2][QB], int) const {}
   __device__ __forceinline__ void record(int, bool, const float (&)[QB], int, int, bool) {}
 };
 
@@ -251,21 +251,25 @@ struct NmFilter {
     row_base = ((int64_t)u.b * a.g.Hq + u.hq) * a.g.Sq;
   }
 
-  // keep bit (kb*16 + r) of bits[qb]: key not masked and (dense, or top-n of its group).  The
-  // ranks are sign-bit arithmetic per element; the sink/recent windows and masked keys are key
-  // ranges, turned into bit ranges (bits_below) on the few tiles per row that touch them.
-  __device__ __forceinline__ void filter(const KeyTiles<QB>& kt, int j, const f32x16 (&s)[2][QB],
-                                         uint32_t (&bits)[QB], int lane) const {
+  // The rank path: a key is dropped (-inf) unless it is among the top n of its group or lies in
+  // the sink/recent window.  The ranks are sign-bit arithmetic per element, exact for ties; the
+  // windows are key ranges, turned into bit ranges (bits_below) on the few tiles per row that
+  // touch them.  Masked keys are -inf already and stay so.  Each group is decided and applied
+  // before the next is ranked (for M = 8 the other half of a group sits in lane ^ 32, whose
+  // elements of that group are untouched until the same step).
+  __device__ __forceinline__ void rank_apply(const KeyTiles<QB>& kt, int j, f32x16 (&s)[2][QB],
+                                             int lane) const {
     const int k0 = j * kKeysPerTile;
-    const int Sk = kt.Sk, wrow0 = kt.wrow0, h = kt.h;
-    const bool any_masked =
-        (k0 + kKeysPerTile > Sk) || (kt.causal && k0 + kKeysPerTile - 1 > wrow0);
-    const bool any_dense = k0 < sink ||
-        (recent > 0 && k0 <= wrow0 + RW - 1 && k0 + kKeysPerTile - 1 > wrow0 - recent);
+    const int wrow0 = kt.wrow0, h = kt.h;
+    const bool any_dense = dense_tile(kt, k0);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int row = wrow0 + qb * 32 + kt.r32;
-      uint32_t kb_bits = 0u;
+      uint32_t win = 0u;
+      if (any_dense) {   // key < sink, or row - recent < key <= row
+        win = bits_below(sink - k0, h);
+        if (recent > 0) win |= bits_below(row - k0 + 1, h) & ~bits_below(row - recent - k0 + 1, h);
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -280,52 +284,134 @@ struct NmFilter {
           int rank[4];
           group_ranks<M>(own, oth, h == 0, rank);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)   // top-n: rank - n < 0
-            kb_bits |= ((uint32_t)(rank[e] - n) >> 31) << (kb * 16 + 4 * gi + e);
+          for (int e = 0; e < 4; ++e) {
+            const bool keep = rank[e] < n || ((win >> (kb * 16 + 4 * gi + e)) & 1u);
+            s[kb][qb][4 * gi + e] = keep ? s[kb][qb][4 * gi + e] : -INFINITY;
+          }
           // one group at a time: the scheduler would otherwise interleave all eight groups'
           // comparisons and run out of registers
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (any_dense) {   // key < sink, or row - recent < key <= row
-        kb_bits |= bits_below(sink - k0, h);
-        if (recent > 0) kb_bits |= bits_below(row - k0 + 1, h) & ~bits_below(row - recent - k0 + 1, h);
-      }
-      if (any_masked)    // key < Sk and (causal) key <= row
-        kb_bits &= bits_below(kt.causal ? min(Sk, row + 1) - k0 : Sk - k0, h);
-      bits[qb] = kb_bits;
-      if (keep_bits != nullptr || scores != nullptr) export_row(kt, k0, row, qb, kb_bits, s, lane);
     }
   }
 
-  // debug exports of one query row: keep-bit words and raw scores
-  __device__ __forceinline__ void export_row(const KeyTiles<QB>& kt, int k0, int row, int qb,
-                                             uint32_t kb_bits, const f32x16 (&s)[2][QB],
-                                             int lane) const {
-    // lanes l and l^32 hold the same row: both stay active through the swap
-    const int64_t rbase = row_base + row;
-    const int Sk = kt.Sk, h = kt.h;
+  // some row of this wave has a sink or recent-window key in the tile
+  __device__ __forceinline__ bool dense_tile(const KeyTiles<QB>& kt, int k0) const {
+    return k0 < sink ||
+           (recent > 0 && k0 <= kt.wrow0 + RW - 1 && k0 + kKeysPerTile - 1 > kt.wrow0 - recent);
+  }
+
+  // The N-th and (N+1)-th largest of a group of four, t and u.  With a <= b <= c the first three
+  // sorted (min3, med3, max3) and d the fourth: the largest is max(c, d), the 2nd largest
+  // max(b, min(c, d)), the 3rd min(b, max(a, d)) and the smallest min(a, d).
+  template <int N>
+  static __device__ __forceinline__ void nth_largest4(float x0, float x1, float x2, float x3,
+                                                      float& t, float& u) {
+    const float hi = fmaxf(fmaxf(x0, x1), x2);
+    const float lo = fminf(fminf(x0, x1), x2);
+    const float md = __builtin_amdgcn_fmed3f(x0, x1, x2);
+    if constexpr (N == 1) {
+      t = fmaxf(hi, x3);
+      u = fmaxf(md, fminf(hi, x3));
+    } else if constexpr (N == 2) {
+      t = fmaxf(md, fminf(hi, x3));
+      u = fminf(md, fmaxf(lo, x3));
+    } else {
+      t = fminf(md, fmaxf(lo, x3));
+      u = fminf(lo, x3);
+    }
+  }
+
+  // Threshold pass (M = 4): keys below their group's N-th largest t are dropped.  This keeps every
+  // key that reaches t, which is exactly the top N unless the (N+1)-th largest equals t (a tie at
+  // the threshold, decided by the lower key index); such groups set `tie`.
+  template <int N>
+  static __device__ __forceinline__ void threshold_apply(f32x16 (&s)[2][QB], bool& tie) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // this lane's 16 bits sit at key offsets (r/4)*8 + 4h + r%4: spread the nibbles 8 apart,
-      // then shift by 4h; merged with lane^32's half
-      const uint32_t x = (kb_bits >> (kb * 16)) & 0xFFFFu;
-      uint32_t word = ((x & 0xFu) | ((x & 0xF0u) << 4) | ((x & 0xF00u) << 8) |
-                       ((x & 0xF000u) << 12)) << (4 * h);
-      word |= __float_as_uint(other_half(__uint_as_float(word), lane));
-      if (row < kt.Sq) {
-        if (keep_bits != nullptr && h == 0 && k0 + kb * 32 < Sk)
-          keep_bits[rbase * W + k0 / 32 + kb] = word;
-        if (scores != nullptr) {
-          int kbase = k0 + 4 * h;   // key = kbase + c, c a compile-time constant
-          asm volatile("" : "+v"(kbase));
-          float* dst = scores + rbase * Sk + kbase;
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
-            if (kbase + c < Sk) dst[c] = s[kb][qb][r];
-          }
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          f32x16& v = s[kb][qb];
+          float t, u;
+          nth_largest4<N>(v[4 * gi], v[4 * gi + 1], v[4 * gi + 2], v[4 * gi + 3], t, u);
+          tie = tie || (u == t && t != -INFINITY);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * gi + e] = v[4 * gi + e] < t ? -INFINITY : v[4 * gi + e];
+          __builtin_amdgcn_sched_barrier(0);   // one group at a time (register pressure)
         }
+  }
+
+  // Drops the keys the rule does not keep by setting their scores to -inf (masked keys already
+  // are).  M = 4 on a tile without window keys: the threshold pass, then, only if some group of
+  // the wave had a tie at its threshold, the rank pass over the result.  That is exact: the keys
+  // the threshold pass dropped lie below the N-th largest, so they are not in the top N either,
+  // and the rank pass ranks the surviving keys as it would rank them among all.  Tiles touching a
+  // window and M = 8 take the rank pass directly.
+  __device__ __forceinline__ void filter(const KeyTiles<QB>& kt, int j, f32x16 (&s)[2][QB],
+                                         int lane) const {
+    const int k0 = j * kKeysPerTile;
+    if (scores != nullptr) export_scores(kt, k0, s);
+    bool exact = true;
+    if constexpr (M == 4) {
+      if (!dense_tile(kt, k0)) {
+        bool tie = false;
+        if (n == 1) threshold_apply<1>(s, tie);
+        else if (n == 2) threshold_apply<2>(s, tie);
+        else if (n == 3) threshold_apply<3>(s, tie);
+        exact = __builtin_amdgcn_ballot_w64(tie) != 0ull;   // n == 4 keeps every allowed key
+      }
+    }
+    if (exact) rank_apply(kt, j, s, lane);
+    if (keep_bits != nullptr) export_bits(kt, k0, s, lane);
+  }
+
+  // debug export: the raw scores the ranking used (before any key is dropped)
+  __device__ __forceinline__ void export_scores(const KeyTiles<QB>& kt, int k0,
+                                                const f32x16 (&s)[2][QB]) const {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = kt.wrow0 + qb * 32 + kt.r32;
+      if (row >= kt.Sq) continue;
+      int kbase = k0 + 4 * kt.h;   // key = kbase + c, c a compile-time constant
+      asm volatile("" : "+v"(kbase));
+      float* dst = scores + (row_base + row) * kt.Sk + kbase;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+          if (kbase + c < kt.Sk) dst[c] = s[kb][qb][r];
+        }
+    }
+  }
+
+  // debug export: keep-bit words of one tile (a key is kept when its score survived as finite)
+  __device__ __forceinline__ void export_bits(const KeyTiles<QB>& kt, int k0,
+                                              const f32x16 (&s)[2][QB], int lane) const {
+    const int h = kt.h;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = kt.wrow0 + qb * 32 + kt.r32;
+      uint32_t kb_bits = 0u;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          kb_bits |= (s[kb][qb][r] != -INFINITY ? 1u : 0u) << (kb * 16 + r);
+      // lanes l and l^32 hold the same row: both stay active through the swap
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        // this lane's 16 bits sit at key offsets (r/4)*8 + 4h + r%4: spread the nibbles 8 apart,
+        // then shift by 4h; merged with lane^32's half
+        const uint32_t x = (kb_bits >> (kb * 16)) & 0xFFFFu;
+        uint32_t word = ((x & 0xFu) | ((x & 0xF0u) << 4) | ((x & 0xF00u) << 8) |
+                         ((x & 0xF000u) << 12)) << (4 * h);
+        word |= __float_as_uint(other_half(__uint_as_float(word), lane));
+        if (row < kt.Sq && h == 0 && k0 + kb * 32 < kt.Sk)
+          keep_bits[(row_base + row) * W + k0 / 32 + kb] = word;
       }
     }
   }
@@ -370,9 +456,8 @@ struct NmPolicy : KeyTiles<QB> {
     this->init_tiles(a.g, u, D, lane);
     nm.init(a, u);
   }
-  __device__ __forceinline__ void filter(int j, const f32x16 (&s)[2][QB], uint32_t (&bits)[QB],
-                                         int lane) const {
-    nm.filter(*this, j, s, bits, lane);
+  __device__ __forceinline__ void filter(int j, f32x16 (&s)[2][QB], int lane) const {
+    nm.filter(*this, j, s, lane);
   }
   __device__ __forceinline__ void finish(const NmArgs& a, const TileUnit& u, int tid) const {
     nm.finish(a, u, tid);
@@ -390,9 +475,8 @@ struct SkipNmPolicy : SkipDecision<D, NW, QB> {
     SkipDecision<D, NW, QB>::init(a, u, lane);
     nm.init(a, u);
   }
-  __device__ __forceinline__ void filter(int j, const f32x16 (&s)[2][QB], uint32_t (&bits)[QB],
-                                         int lane) const {
-    nm.filter(*this, j, s, bits, lane);
+  __device__ __forceinline__ void filter(int j, f32x16 (&s)[2][QB], int lane) const {
+    nm.filter(*this, j, s, lane);
   }
   __device__ __forceinline__ void finish(const SkipNmArgs& a, const TileUnit& u, int tid) const {
     SkipDecision<D, NW, QB>::finish(a, u, tid);

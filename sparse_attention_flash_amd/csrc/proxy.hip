@@ -57,7 +57,7 @@ struct ExactPolicy {
   __device__ __forceinline__ bool negligible(const float (&)[QB], const float (&)[QB], int) const {
     return false;
   }
-  __device__ __forceinline__ void filter(int, const f32x16 (&)[2][QB], uint32_t (&)[QB], int) const {}
+  __device__ __forceinline__ void filter(int, f32x16 (&)[2][QB], int) const {}
   __device__ __forceinline__ void record(int, bool, const float (&)[QB], int, int, bool) {}
 };
 
@@ -187,8 +187,6 @@ void proxy_kernel(ProxyArgs a) {
       sp.mask(t, s);
       TileState<QB> ts;
       tile_row_max<QB>(s, g.c32, ts.M);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) ts.kbits[qb] = ~0u;
       ts.keep = true;
       softmax_pv<D, QB>(sp, t, s, ts, mref, l, o, sm.v[0], g.c32, lane);
     }
