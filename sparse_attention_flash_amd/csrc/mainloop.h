@@ -117,7 +117,7 @@ __device__ __forceinline__ void tile_row_max(const f32x16 (&s)[2][QB], float c32
   }
 }
 
-// Per-tile state: row maxima (log2 domain), N:M keep bits, decision.
+// Per-tile state: row maxima (log2 domain) and the decision.
 template <int QB>
 struct TileState {
   float M[QB];
@@ -126,9 +126,9 @@ struct TileState {
 
 // Softmax of a kept tile fused with its P.V product.  For each 16-key chunk: exponentials of the
 // chunk (VALU), then the MFMAs that consume them, so the VALU work of one chunk overlaps the MFMAs
-// of the previous one.  Keys a filter dropped (N:M) arrive as -inf and get weight 0;
-// Pol::weight (proxy) scales each key's row-sum term.  The row sum adds the fp32 weights (before their rounding to bf16 for P.V), which
-// keeps the LSE at fp32 accuracy.
+// of the previous one.  Keys a filter dropped (N:M) arrive as -inf and get weight 0; Pol::weight
+// (proxy) scales each key's row-sum term.  The row sum adds the fp32 weights (before their
+// rounding to bf16 for P.V), which keeps the LSE at fp32 accuracy.
 template <int D, int QB, class Pol>
 __device__ __forceinline__ void softmax_pv(const Pol& pol, int step, const f32x16 (&s)[2][QB],
                                            const TileState<QB>& ts, float (&mref)[QB],
