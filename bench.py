@@ -116,6 +116,20 @@ def time_steps(torch, fn, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
+def time_ab(torch, arms, steps, warmup, rounds=5):
+    """Balanced interleaved A/B timing: `rounds` rounds, each timing every arm for `steps` calls in
+    turn (after `warmup` calls of each arm); returns each arm's median per-call ms over the rounds."""
+    for fn in arms.values():
+        for _ in range(warmup):
+            fn()
+    res = {name: [] for name in arms}
+    for r in range(rounds):
+        order = list(arms) if r % 2 == 0 else list(reversed(list(arms)))
+        for name in order:
+            res[name].append(time_steps(torch, arms[name], steps, 1))
+    return {name: float(np.median(v)) for name, v in res.items()}
+
+
 def source_digest(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -255,8 +269,21 @@ def run_paths(torch, sa, W, to_dev, steps, warmup):
     except sa.SaError as e:
         out["llm_decode_gqa_kv8192"] = {"unavailable": str(e)}
 
-    # proxy-compensated block-sparse attention with bitmask routes
-    wl = W.WORKLOADS["proxy_bitmask_s16257"]
+    # proxy-compensated block-sparse attention with bitmask routes, at the survey's workload and at
+    # the shape of the pages' B200 A/B (context)
+    for name in ("proxy_bitmask_s16257", "proxy_page_s32760"):
+        out[name] = proxy_leg(torch, sa, W, to_dev, W.WORKLOADS[name], steps, warmup)
+    out["proxy_page_s32760"]["context_b200_pages"] = {
+        "note": "NVIDIA B200, FlashInfer block-sparse wrapper; other hardware, context only",
+        "wrapper_ms_off_on": [1.3172, 1.4298], "attention_ms_off_on": [1.1261, 1.2121],
+        "prep_ms_off_on": [0.0145, 0.0176]}
+    return out
+
+
+def proxy_leg(torch, sa, W, to_dev, wl, steps, warmup):
+    """Route prep and proxy forward (proxy off / on) on one workload; "wrapper" = prep + forward,
+    as the pages time their run call."""
+    dev = torch.device("cuda:0")
     q, k, v = wl.generate()
     B, S, H, D = q.shape
     Bq, Bk = wl.block_q, wl.block_k
@@ -270,7 +297,8 @@ def run_paths(torch, sa, W, to_dev, steps, warmup):
     n_exact = torch.empty((B, H, nQB), dtype=torch.int32, device=dev)
     idx = torch.empty((B, H, nQB, nKB), dtype=torch.int32, device=dev)
     keep = torch.empty_like(bmd)
-    rec = {"exact_blocks_per_row": n_set, "n_kv_blocks": nKB}
+    rec = {"shape": [B, S, H, D], "block_q": Bq, "block_k": Bk, "exact_blocks_per_row": n_set,
+           "n_kv_blocks": nKB}
     try:
         def prep():
             sa.sa_bitmask_route_prep(bmd, n_exact, idx, keep, batch=B, heads_kv=H, seqlen_q=S,
@@ -284,17 +312,27 @@ def run_paths(torch, sa, W, to_dev, steps, warmup):
         exact_tokens = np.where(ix >= 0, lens[np.clip(ix, 0, None)], 0).sum(-1)   # [B,H,nQB]
         exact_flops = int(4 * D * (exact_tokens * rows[None, None]).sum())
         proxy_flops = int(4 * D * ((nKB - ne) * rows[None, None]).sum())
+        def fwd(use):
+            sa.sa_proxy_block_sparse_fwd(qd, kd, vd, kmd, vsd, n_exact, idx, keep, use, o,
+                                         block_q=Bq, block_k=Bk)
+
+        def wrapper(use):
+            prep()
+            fwd(use)
+        # the pages' method: balanced, interleaved rounds per arm
+        t = time_ab(torch, {"off": lambda: fwd(0), "on": lambda: fwd(1),
+                            "w_off": lambda: wrapper(0), "w_on": lambda: wrapper(1)},
+                    steps, warmup)
         for name, use in (("proxy_off", 0), ("proxy_on", 1)):
-            ms = time_steps(torch, lambda: sa.sa_proxy_block_sparse_fwd(
-                qd, kd, vd, kmd, vsd, n_exact, idx, keep, use, o, block_q=Bq, block_k=Bk),
-                steps, warmup)
+            ms, ms_w = t["on" if use else "off"], t["w_on" if use else "w_off"]
             fl = exact_flops + (proxy_flops if use else 0)
-            rec[name] = {"ms": round(ms, 4), "computed_tflops": round(fl / ms / 1e9, 2)}
+            rec[name] = {"ms": round(ms, 4), "wrapper_ms": round(ms_w, 4),
+                         "computed_tflops": round(fl / ms / 1e9, 2)}
         rec["proxy_overhead"] = round(rec["proxy_on"]["ms"] / rec["proxy_off"]["ms"] - 1, 4)
+        rec["timing"] = "median of 5 balanced interleaved rounds per arm"
     except sa.SaError as e:
         rec["unavailable"] = str(e)
-    out[wl.name] = rec
-    return out
+    return rec
 
 
 def decode_path(torch, sa, W, to_dev, steps, warmup, profile=False):
@@ -362,6 +400,27 @@ def decode_path(torch, sa, W, to_dev, steps, warmup, profile=False):
 
 
 # ------------------------------------------------------------------------------------------------
+def speedup_curve(torch, sa, W, qd, kd, vd, o, st, wl, P, D, ms0, steps, warmup):
+    """The headline kernel over a range of thresholds: tile sparsity, time, computed TFLOP/s and
+    speedup against the same kernel at lambda = 0 (untimed by the headline value)."""
+    S = qd.shape[1]
+    lams = [0.1, 0.2, 0.3, 0.5, 0.7, 1.5, 3.0]
+    for target in (0.5, 0.7):
+        lams.append(sa.sa_threshold_from_calib(W.CALIB_A, W.CALIB_B, target, S)[1])
+    rows = []
+    for lam in sorted(lams):
+        ms = time_steps(torch, lambda: sa.sa_skip_softmax_fwd(
+            qd, kd, vd, o, lam, causal=wl.causal, block_q=wl.block_q, block_k=wl.block_k,
+            tile_state=st), steps, warmup)
+        ts = st.cpu().numpy()
+        computed, _ = skip_flops(ts, P, D)
+        rows.append({"lambda": round(lam, 6),
+                     "tile_sparsity": round(float((ts == 1).sum() / max(1, (ts != 2).sum())), 4),
+                     "ms": round(ms, 4), "computed_tflops": round(computed / ms / 1e9, 2),
+                     "speedup_vs_lambda0": round(ms0 / ms, 3)})
+    return rows
+
+
 def calibration(sa, W, qd, kd, vd, o, cnt, wl, S):
     """Calibration sweep over the pages' trial thresholds on the headline workload, the log-space
     fit of the measured sparsities, and the sparsity reached when targets are lowered through the
@@ -488,6 +547,8 @@ def main():
                   "between steps",
     }
     if not args.no_paths:
+        result["speedup_curve"] = speedup_curve(torch, sa, W, qd, kd, vd, o, st, wl, P, D, ms0,
+                                                args.steps, args.warmup)
         result["calibration"] = calibration(sa, W, qd, kd, vd, o, cnt, wl, S)
         del qd, kd, vd, o
         torch.cuda.empty_cache()

@@ -337,4 +337,7 @@ WORKLOADS = {
                                        ("ragged", True))),
     "proxy_bitmask_s16257": Workload("proxy_bitmask_s16257", "proxy", 1, 24, 24, 16257, 128, False,
                                      128, 128, "iid", 5, (("density", 0.25),)),
+    # the shape of the pages' proxy A/B: [1, 32760, 12, 128], 64-token blocks, 84 of 512 exact
+    "proxy_page_s32760": Workload("proxy_page_s32760", "proxy", 1, 12, 12, 32760, 128, False,
+                                  64, 64, "iid", 5, (("density", 84 / 512),)),
 }
