@@ -69,8 +69,8 @@ struct Dma {
   static constexpr int kPerWave = L::kBlocks / NW;   // one block (1 KiB) per wave-wide instruction
   static_assert(kPerWave >= 1 && L::kBlocks % NW == 0, "tile must split over the waves");
 
-  // Lane byte offset of a block copy relative to the block's first row (the same for every block:
-  // the row shift of block b goes into the buffer resource base).
+  // Lane byte offset of a block copy relative to the block's first row (the same for every block;
+  // the copy adds the block's row shift).
   struct LaneOffsets {
     int off;
   };
@@ -89,16 +89,22 @@ struct Dma {
   static __device__ __forceinline__ void copy(char* lds, const __bf16* base, int bytes,
                                               int stride_b, const LaneOffsets& lo, int wave) {
     const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, max(0, bytes),
+                                                        0x00020000);
+    // One resource per tile; a block's row shift goes into the lane offset, so the per-lane
+    // range check still zero-fills rows past the end.  The empty asm makes the block offsets
+    // look loop-variant: hoisted out of the key loop they would hold about 30 SGPRs, which the
+    // compiler then spills to VGPR lanes and reloads (v_readlane) in front of every copy.
+    int w = wave, sb = stride_b;
+    asm volatile("" : "+s"(w), "+s"(sb));
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
-      const int blk = wave + i * NW;
-      const int shift = blk * L::kRowShiftPerBlock * stride_b;   // uniform
-      const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)((const char*)base + shift), (short)0, max(0, bytes - shift), 0x00020000);
+      const int blk = w + i * NW;
+      const int voff = lo.off + blk * L::kRowShiftPerBlock * sb;
       const unsigned dst = lds0 + blk * L::kPitch;
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                    :
-                   : "s"(dst), "v"(lo.off), "s"(rsrc)
+                   : "s"(dst), "v"(voff), "s"(rsrc)
                    : "memory", "m0");
     }
   }

@@ -65,8 +65,8 @@ struct TileLayout<128, kV> {
   static constexpr int kPitch = kV ? 1088 : 1040;   // bytes per block
   static constexpr int kBlocks = 16;
   static constexpr int kBytes = kBlocks * kPitch;
-  // A copy of block b: lane l fetches row b + 16*(l/16), chunk l%16; the row shift b goes into
-  // the buffer resource base.
+  // A copy of block b: lane l fetches row b + 16*(l/16), chunk l%16 (dma_lane plus the row shift
+  // of b).
   static constexpr int kRowShiftPerBlock = 1;
   static __device__ __forceinline__ int dma_lane(int stride_b, int lane) {
     return (lane >> 4) * 16 * stride_b + (lane & 15) * 16;
