@@ -206,6 +206,225 @@ void proxy_kernel(ProxyArgs a) {
   store_o<D, QB>(op, g.os[1], g.Sq - wrow0, o, inv, lane);
 }
 
+// ---- 64-row query blocks: copy waves and compute waves ------------------------------------------
+// A 64-row block has two compute waves, and on those the K/V copies of every tile (16 per wave)
+// took a large share of the time: each copy stalls its wave at issue while the vector-memory path
+// is busy.  Here a workgroup of 8 waves takes two query blocks of the same (batch, query head),
+// each with its own double-buffered K/V tiles (2 x 68 KB of LDS, one workgroup per CU).  Waves 0-3
+// compute (two per query block) and waves 4-7 only copy (two per query block); waves w and w + 4
+// share a SIMD, so every SIMD holds one compute wave and one copy wave.  Both blocks advance in
+// lockstep through one barrier per step; the block with fewer exact tiles idles at the end.
+//
+//   copy waves:    K(0), V(0), K(1); wait K(0); barrier 0;
+//                  step j: wait V(j), K(j+1); barrier j+1; request V(j+1), K(j+2)
+//   compute waves: barrier 0; S(0);
+//                  step j: barrier j+1; softmax(j) + O += P(j) V(j); S(j+1)
+// At barrier j+1 the compute waves are done with V(j-1) and K(j), the buffers the copies that
+// follow it overwrite.  The summary tiles (proxy on) follow in a loop of their own, double-buffered
+// the same way with one barrier per tile.
+constexpr int kPcGroups = 2;   // query blocks per workgroup
+constexpr int kPcWaves = 2;    // compute (and copy) waves per query block
+
+template <int D>
+__global__ __launch_bounds__(2 * kPcGroups * kPcWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void proxy_pc_kernel(ProxyArgs a) {
+  constexpr int QB = 1;
+  constexpr int BR = kPcWaves * 32;   // rows per query block
+  using DmaK = Dma<KLayout<D>, kPcWaves>;
+  using DmaV = Dma<VLayout<D>, kPcWaves>;
+  constexpr int kN = DmaK::kPerWave;
+  static_assert(DmaV::kPerWave == kN, "K and V tiles take the same number of copies");
+  __shared__ __attribute__((aligned(1024))) Smem<D, kPcWaves> sms[kPcGroups];
+
+  const AttnGeom& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool copier = wave >= kPcGroups * kPcWaves;
+  const int cw = copier ? wave - kPcGroups * kPcWaves : wave;
+  const int grp = cw / kPcWaves, rank = cw % kPcWaves;
+  Smem<D, kPcWaves>& sm = sms[grp];
+  const int h = lane >> 5, r32 = lane & 31;
+  const int Bk = g.block_k;
+  const int nQB = (g.Sq + BR - 1) / BR;
+  const int nPair = (nQB + kPcGroups - 1) / kPcGroups;
+  const int nKB = (g.Sk + Bk - 1) / Bk;
+  const int Wd = (nKB + 31) / 32;
+  const int G = g.Hq / g.Hkv;
+  const int total = g.B * g.Hq * nPair;
+
+  int item = xcd_remap(blockIdx.x, total);
+  const int gq = item % G;
+  item /= G;
+  const int pair = item % nPair;
+  item /= nPair;
+  const int hk = item % g.Hkv;
+  const int b = item / g.Hkv;
+  const int hq = hk * G + gq;
+
+  const int qblk = pair * kPcGroups + grp;
+  const bool present = qblk < nQB;   // the last pair may have one block
+  const int row0 = qblk * BR;
+  const int wrow0 = row0 + rank * 32;
+  const int64_t route_row = ((int64_t)b * g.Hkv + hk) * nQB + min(qblk, nQB - 1);
+
+  ExactPolicy<D, kPcWaves, QB> pol;
+  pol.kslab = (const __bf16*)g.k + b * g.ks[0] + hk * g.ks[2];
+  pol.vslab = (const __bf16*)g.v + b * g.vs[0] + hk * g.vs[2];
+  pol.exact = a.exact_idx + route_row * nKB;
+  pol.k_stride_b = (int)(g.ks[1] * 2);
+  pol.v_stride_b = (int)(g.vs[1] * 2);
+  pol.k_bytes = (int)(((int64_t)(g.Sk - 1) * g.ks[1] + D) * 2);
+  pol.v_bytes = (int)(((int64_t)(g.Sk - 1) * g.vs[1] + D) * 2);
+  pol.Sk = g.Sk;
+  pol.Bk = Bk;
+  pol.sub = Bk / kKeysPerTile;
+  // never index past the route row, whatever the caller passed
+  pol.n_exact = present ? min(max(__builtin_amdgcn_readfirstlane(a.n_exact[route_row]), 0), nKB) : 0;
+  pol.h = h;
+  const int n = pol.steps();
+  // steps of the other query block of the pair (both walk max(n, n_other) barriers)
+  int n_other = 0;
+  {
+    const int oblk = pair * kPcGroups + (grp ^ 1);
+    if (oblk < nQB) {
+      const int64_t orow = ((int64_t)b * g.Hkv + hk) * nQB + oblk;
+      n_other = min(max(__builtin_amdgcn_readfirstlane(a.n_exact[orow]), 0), nKB) * pol.sub;
+    }
+  }
+  const int N = max(n, n_other);
+  const int n_sum = a.use_proxy ? (nKB + kKeysPerTile - 1) / kKeysPerTile : 0;
+
+  if (copier) {
+    auto issue_k = [&](int step) {
+      const TileSrc t = pol.src(step);
+      DmaK::copy(sm.k[step & 1], t.k, t.k_bytes, t.k_stride_b,
+                 DmaK::lane_offsets(t.k_stride_b, rank, lane), rank);
+    };
+    auto issue_v = [&](int step) {
+      const TileSrc t = pol.src(step);
+      DmaV::copy(sm.v[step & 1], t.v, t.v_bytes, t.v_stride_b,
+                 DmaV::lane_offsets(t.v_stride_b, rank, lane), rank);
+    };
+    if (n > 0) {
+      issue_k(0);
+      issue_v(0);
+    }
+    if (n > 1) {
+      issue_k(1);
+      wait_vmcnt<2 * kN>();   // K(0) landed
+    } else {
+      wait_vmcnt<kN>();
+    }
+    lds_barrier();
+    for (int j = 0; j < N; ++j) {
+      wait_vmcnt<0>();   // V(j), K(j+1)
+      lds_barrier();
+      if (j + 1 < n) issue_v(j + 1);
+      if (j + 2 < n) issue_k(j + 2);
+    }
+    if (n_sum > 0) {
+      // summary tile t (64 rows of k_mean / v_sum) into buffer t&1
+      const int64_t sbase = ((int64_t)b * g.Hkv + hk) * nKB * D;
+      const auto sklo = DmaK::lane_offsets(D * 2, rank, lane);
+      const auto svlo = DmaV::lane_offsets(D * 2, rank, lane);
+      auto issue_s = [&](int t) {
+        if (!present) return;
+        const int r0 = t * kKeysPerTile;
+        const int bytes = (nKB - r0) * D * 2;   // rows past nKB read as zeros (and are masked)
+        DmaK::copy(sm.k[t & 1], (const __bf16*)a.k_mean + sbase + (int64_t)r0 * D, bytes, D * 2,
+                   sklo, rank);
+        DmaV::copy(sm.v[t & 1], (const __bf16*)a.v_sum + sbase + (int64_t)r0 * D, bytes, D * 2,
+                   svlo, rank);
+      };
+      lds_barrier();   // the compute waves are done with every exact tile
+      issue_s(0);
+      if (n_sum > 1) {
+        issue_s(1);
+        wait_vmcnt<2 * kN>();   // tile 0 landed
+      } else {
+        wait_vmcnt<0>();
+      }
+      lds_barrier();
+      for (int t = 1; t < n_sum; ++t) {
+        wait_vmcnt<0>();   // tile t
+        lds_barrier();     // the compute waves are done with tile t-1
+        if (t + 1 < n_sum) issue_s(t + 1);
+      }
+    }
+    return;
+  }
+
+  const auto qsrc = slab_rsrc((const __bf16*)g.q + b * g.qs[0] + hq * g.qs[2], g.qs[1], g.Sq, D);
+  bf16x8 qf[QB][D / 16];
+  load_q_frags<D, QB>(qf, qsrc, g.qs[1], wrow0, lane);
+
+  f32x16 o[D / 32][QB];
+  float mref[QB], l[QB];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db][0] = f32x16{};
+  mref[0] = -INFINITY;
+  l[0] = 0.f;
+
+  f32x16 s[2][QB];
+  TileState<QB> ts;
+  auto scores = [&](int step) {
+    qk_tile<D, QB>(sm.k[step & 1], qf, s, lane);
+    pol.mask(step, s, lane);
+    tile_row_max<QB>(s, g.c32, ts.M);
+    ts.keep = true;
+  };
+  lds_barrier();
+  if (n > 0) scores(0);
+  for (int j = 0; j < N; ++j) {
+    lds_barrier();
+    if (j < n) softmax_pv<D, QB>(pol, j, s, ts, mref, l, o, sm.v[j & 1], g.c32, lane);
+    if (j + 1 < n) scores(j + 1);
+  }
+
+  if (n_sum > 0) {
+    SummaryPolicy<QB> sp;
+    sp.keep = a.proxy_keep + route_row * Wd;
+    sp.Bk = Bk;
+    sp.nKB = nKB;
+    sp.Wd = Wd;
+    sp.last_len = g.Sk - (nKB - 1) * Bk;
+    sp.h = h;
+    lds_barrier();
+    for (int t = 0; t < n_sum; ++t) {
+      lds_barrier();   // summary tile t has landed
+      if (present) {
+        qk_tile<D, QB>(sm.k[t & 1], qf, s, lane);
+        sp.mask(t, s);
+        tile_row_max<QB>(s, g.c32, ts.M);
+        ts.keep = true;
+        softmax_pv<D, QB>(sp, t, s, ts, mref, l, o, sm.v[t & 1], g.c32, lane);
+      }
+    }
+  }
+  if (!present) return;
+
+  const float lt = half_sum(l[0]);
+  float inv[QB];
+  inv[0] = lt > 0.f ? 1.f / lt : 0.f;
+  const int row = wrow0 + r32;
+  if (a.lse != nullptr && h == 0 && row < g.Sq)
+    a.lse[((int64_t)b * g.Hq + hq) * g.Sq + row] =
+        lt > 0.f ? (mref[0] + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
+  __bf16* op = (__bf16*)g.o + b * g.os[0] + (int64_t)wrow0 * g.os[1] + hq * g.os[2];
+  store_o<D, QB>(op, g.os[1], g.Sq - wrow0, o, inv, lane);
+}
+
+template <int D>
+hipError_t launch_pc(const ProxyArgs& a, hipStream_t stream) {
+  constexpr int BR = kPcWaves * 32;
+  const int nQB = (a.g.Sq + BR - 1) / BR;
+  const int nPair = (nQB + kPcGroups - 1) / kPcGroups;
+  const int total = a.g.B * a.g.Hq * nPair;
+  hipLaunchKernelGGL((proxy_pc_kernel<D>), dim3(total), dim3(2 * kPcGroups * kPcWaves * 64), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
 template <int D, int NW, int QB>
 hipError_t launch_t(const ProxyArgs& a, hipStream_t stream) {
   constexpr int BR = NW * 32 * QB;
@@ -220,9 +439,8 @@ hipError_t launch_t(const ProxyArgs& a, hipStream_t stream) {
 hipError_t launch_proxy(const ProxyArgs& a, hipStream_t stream) {
   constexpr int QB = kQueryBlocksPerWave;
   const bool q128 = a.g.block_q == 128;
-  if (a.g.D == 128)
-    return q128 ? launch_t<128, 4 / QB, QB>(a, stream) : launch_t<128, 2 / QB, QB>(a, stream);
-  return q128 ? launch_t<64, 4 / QB, QB>(a, stream) : launch_t<64, 2 / QB, QB>(a, stream);
+  if (a.g.D == 128) return q128 ? launch_t<128, 4 / QB, QB>(a, stream) : launch_pc<128>(a, stream);
+  return q128 ? launch_t<64, 4 / QB, QB>(a, stream) : launch_pc<64>(a, stream);
 }
 
 }  // namespace sa

@@ -239,9 +239,10 @@ def test_skip_nm_full_size():
     assert_output_parity(got[valid], o_ref[valid], "skip + 2:4 O")
 
 
-def test_proxy_full_size():
-    wl = W.WORKLOADS["proxy_bitmask_s16257"]
-    announce("proxy full size")
+@pytest.mark.parametrize("name", ["proxy_bitmask_s16257", "proxy_page_s32760"])
+def test_proxy_full_size(name):
+    wl = W.WORKLOADS[name]
+    announce(f"proxy full size {name}")
     q, k, v = wl.generate()
     B, S, H, D = q.shape
     Bq, Bk = wl.block_q, wl.block_k

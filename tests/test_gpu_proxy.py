@@ -120,6 +120,8 @@ def run_proxy(q, k, v, bm, Bq, Bk, use_proxy):
     (1, 257, 2, 2, 128, 64, 64, 0.4),
     (2, 1000, 2, 2, 64, 128, 64, 0.25),
     (1, 2049, 4, 2, 128, 128, 128, 0.25),
+    (1, 1000, 2, 2, 64, 64, 64, 0.25),      # head_dim 64, 64-row blocks, even block count
+    (2, 777, 4, 2, 128, 64, 128, 0.3),      # 64-row blocks over 128-key blocks, odd block count
 ])
 def test_proxy_parity(cfg, use_proxy):
     B, S, Hq, Hkv, D, Bq, Bk, dens = cfg
@@ -130,6 +132,38 @@ def test_proxy_parity(cfg, use_proxy):
     o, lse, o_ref, lse_ref = run_proxy(q, k, v, bm, Bq, Bk, use_proxy)
     assert_output_parity(o, o_ref, f"proxy {cfg}")
     lmx, _ = err(lse, lse_ref)
+    assert lmx < 2e-3
+
+
+@pytest.mark.parametrize("use_proxy", [0, 1])
+@pytest.mark.parametrize("D", [64, 128])
+def test_proxy_uneven_routes(D, use_proxy):
+    """64-row query blocks run two to a workgroup in lockstep: rows of very different exact-block
+    counts (none, a few, all) side by side, and an odd number of query blocks."""
+    B, S, H, Bq, Bk = 1, 1100, 2, 64, 64
+    announce(f"proxy uneven routes D={D} use_proxy={use_proxy}")
+    q, k, v = W.gen_iid(56, B, S, S, H, H, D)
+    nQB, nKB = -(-S // Bq), -(-S // Bk)
+    rng = np.random.default_rng(56)
+    bits = np.zeros((B, H, nQB, nKB), bool)
+    for hh in range(H):
+        for qb in range(nQB):
+            kind = (qb + hh) % 4
+            if kind == 1:
+                bits[0, hh, qb, rng.choice(nKB, 2, replace=False)] = True
+            elif kind == 2:
+                bits[0, hh, qb] = True
+            elif kind == 3:
+                bits[0, hh, qb, rng.choice(nKB, int(rng.integers(3, nKB)), replace=False)] = True
+    W_ = -(-nKB // 32)
+    bm = np.zeros((B, H, nQB, W_), np.uint32)
+    for j in range(nKB):
+        bm[..., j // 32] |= bits[..., j].astype(np.uint32) << np.uint32(j % 32)
+    o, lse, o_ref, lse_ref = run_proxy(q, k, v, bm, Bq, Bk, use_proxy)
+    fin = np.isfinite(lse_ref)
+    assert_output_parity(o, o_ref, f"proxy uneven D={D}")
+    assert (np.isneginf(lse) == ~fin).all()
+    lmx, _ = err(lse[fin], lse_ref[fin])
     assert lmx < 2e-3
 
 
