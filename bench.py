@@ -53,6 +53,9 @@ def parse_args():
                    help="decode kernels only, for profiler runs: warmup + steps decode steps at "
                         "the calibrated-target threshold (no sweep, no other legs); prints their "
                         "timing as one JSON line")
+    p.add_argument("--profile-proxy", default="", metavar="WORKLOAD",
+                   help="proxy leg of one workload only (e.g. proxy_page_s32760), for profiler "
+                        "runs; prints its record as one JSON line")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="only run 5 device-to-device copies of BYTES bytes (a plain copy kernel "
                         "of known size, used to scale the HBM byte counters) and exit")
@@ -471,6 +474,14 @@ def main():
     import workloads as W
 
     dev = torch.device("cuda:0")
+    if args.profile_proxy:
+        def to_dev_p(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+
+        print(json.dumps(proxy_leg(torch, sa, W, to_dev_p, W.WORKLOADS[args.profile_proxy],
+                                   args.steps, args.warmup)))
+        return
 
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
