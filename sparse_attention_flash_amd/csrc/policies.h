@@ -323,6 +323,57 @@ struct NmFilter {
     }
   }
 
+  // The four values sorted, largest first (the same max3 / med3 / min3 construction).
+  static __device__ __forceinline__ void sort4_desc(float x0, float x1, float x2, float x3,
+                                                    float (&a)[4]) {
+    const float hi = fmaxf(fmaxf(x0, x1), x2);
+    const float lo = fminf(fminf(x0, x1), x2);
+    const float md = __builtin_amdgcn_fmed3f(x0, x1, x2);
+    a[0] = fmaxf(hi, x3);
+    a[1] = fmaxf(md, fminf(hi, x3));
+    a[2] = fminf(md, fmaxf(lo, x3));
+    a[3] = fminf(lo, x3);
+  }
+
+  // The K-th largest of the eight values in two lists of four sorted largest first: the maximum
+  // over i of min(a[i-1], b[K-1-i]), with a[-1] = b[-1] = +inf and i from max(0, K-4) to min(K, 4)
+  // (i of the K largest come from a and the rest from b).
+  template <int K>
+  static __device__ __forceinline__ float kth_largest8(const float (&a)[4], const float (&b)[4]) {
+    float t = -INFINITY;
+#pragma unroll
+    for (int i = (K > 4 ? K - 4 : 0); i <= (K < 4 ? K : 4); ++i) {
+      const float x = i == 0 ? INFINITY : a[i > 0 ? i - 1 : 0];
+      const float y = K - 1 - i < 0 ? INFINITY : b[K - 1 - i >= 0 ? K - 1 - i : 0];
+      t = fmaxf(t, fminf(x, y));
+    }
+    return t;
+  }
+
+  // Threshold pass (M = 8): the group's other four keys are the same elements of lane ^ 32.  Each
+  // lane sorts its four, exchanges the sorted four with lane ^ 32 and takes the N-th and (N+1)-th
+  // largest of the eight; then as for M = 4 (both lanes of a group find the same t and u).
+  template <int N>
+  static __device__ __forceinline__ void threshold_apply8(f32x16 (&s)[2][QB], int lane, bool& tie) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          f32x16& v = s[kb][qb];
+          float a[4], b[4];
+          sort4_desc(v[4 * gi], v[4 * gi + 1], v[4 * gi + 2], v[4 * gi + 3], a);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b[e] = other_half(a[e], lane);
+          const float t = kth_largest8<N>(a, b), u = kth_largest8<N + 1>(a, b);
+          tie = tie || (u == t && t != -INFINITY);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * gi + e] = v[4 * gi + e] < t ? -INFINITY : v[4 * gi + e];
+          __builtin_amdgcn_sched_barrier(0);   // one group at a time (register pressure)
+        }
+  }
+
   // Threshold pass (M = 4): keys below their group's N-th largest t are dropped.  This keeps every
   // key that reaches t, which is exactly the top N unless the (N+1)-th largest equals t (a tie at
   // the threshold, decided by the lower key index); such groups set `tie`.
@@ -345,24 +396,35 @@ struct NmFilter {
   }
 
   // Drops the keys the rule does not keep by setting their scores to -inf (masked keys already
-  // are).  M = 4 on a tile without window keys: the threshold pass, then, only if some group of
-  // the wave had a tie at its threshold, the rank pass over the result.  That is exact: the keys
-  // the threshold pass dropped lie below the N-th largest, so they are not in the top N either,
-  // and the rank pass ranks the surviving keys as it would rank them among all.  Tiles touching a
-  // window and M = 8 take the rank pass directly.
+  // are).  On a tile without window keys: the threshold pass, then, only if some group of the wave
+  // had a tie at its threshold, the rank pass over the result.  That is exact: the keys the
+  // threshold pass dropped lie below the N-th largest, so they are not in the top N either, and
+  // the rank pass ranks the surviving keys as it would rank them among all.  Tiles touching a
+  // window take the rank pass directly.
   __device__ __forceinline__ void filter(const KeyTiles<QB>& kt, int j, f32x16 (&s)[2][QB],
                                          int lane) const {
     const int k0 = j * kKeysPerTile;
     if (scores != nullptr) export_scores(kt, k0, s);
     bool exact = true;
-    if constexpr (M == 4) {
-      if (!dense_tile(kt, k0)) {
-        bool tie = false;
+    if (!dense_tile(kt, k0)) {
+      bool tie = false;
+      if constexpr (M == 4) {
         if (n == 1) threshold_apply<1>(s, tie);
         else if (n == 2) threshold_apply<2>(s, tie);
         else if (n == 3) threshold_apply<3>(s, tie);
-        exact = __builtin_amdgcn_ballot_w64(tie) != 0ull;   // n == 4 keeps every allowed key
+      } else {
+        switch (n) {
+          case 1: threshold_apply8<1>(s, lane, tie); break;
+          case 2: threshold_apply8<2>(s, lane, tie); break;
+          case 3: threshold_apply8<3>(s, lane, tie); break;
+          case 4: threshold_apply8<4>(s, lane, tie); break;
+          case 5: threshold_apply8<5>(s, lane, tie); break;
+          case 6: threshold_apply8<6>(s, lane, tie); break;
+          case 7: threshold_apply8<7>(s, lane, tie); break;
+          default: break;
+        }
       }
+      exact = __builtin_amdgcn_ballot_w64(tie) != 0ull;   // n >= M keeps every allowed key
     }
     if (exact) rank_apply(kt, j, s, lane);
     if (keep_bits != nullptr) export_bits(kt, k0, s, lane);

@@ -88,6 +88,20 @@ def test_ties_lower_index_kept():
     assert (g["bits"] == expect).all()
 
 
+@pytest.mark.parametrize("n", [1, 3, 6])
+def test_ties_lower_index_kept_m8(n):
+    """Groups of eight identical keys: every group ties at its threshold, and the lower key indices
+    must win (the two halves of a group sit in lanes l and l ^ 32)."""
+    announce(f"nm ties m=8 n={n}")
+    k1 = W.gen_iid(36, 1, 1, 8, 1, 1, 64)[1]
+    k = np.repeat(k1, 8, axis=1)                 # 64 keys, each group of 8 identical
+    q, _, v = W.gen_iid(36, 1, 64, 64, 1, 1, 64)
+    g = run_gpu(q, k, v, False, 64, n, 8, 0, 0)
+    byte = (1 << n) - 1                          # keys 0..n-1 of every group of 8
+    expect = np.uint32(byte * 0x01010101)
+    assert (g["bits"] == expect).all()
+
+
 def test_n_equals_m_matches_skip_kernel_at_lambda_zero():
     announce("nm N=M vs dense")
     q, k, v = W.gen_llm(35, 1, 384, 2, 2, 128)
