@@ -29,6 +29,26 @@ struct ExactPolicy {
   int k_stride_b, v_stride_b, k_bytes, v_bytes;
   int Sk, Bk, sub, n_exact, h;
 
+  // the route row of query block route_row of (b, KV head hk); a row that is not present (the
+  // missing half of a 64-row pair) has no steps
+  __device__ __forceinline__ void init(const ProxyArgs& a, int b, int hk, int64_t route_row,
+                                       int nKB, int lane_half, bool present = true) {
+    const AttnGeom& g = a.g;
+    kslab = (const __bf16*)g.k + b * g.ks[0] + hk * g.ks[2];
+    vslab = (const __bf16*)g.v + b * g.vs[0] + hk * g.vs[2];
+    exact = a.exact_idx + route_row * nKB;
+    k_stride_b = (int)(g.ks[1] * 2);
+    v_stride_b = (int)(g.vs[1] * 2);
+    k_bytes = (int)(((int64_t)(g.Sk - 1) * g.ks[1] + D) * 2);
+    v_bytes = (int)(((int64_t)(g.Sk - 1) * g.vs[1] + D) * 2);
+    Sk = g.Sk;
+    Bk = g.block_k;
+    sub = Bk / kKeysPerTile;
+    // never index past the route row, whatever the caller passed
+    n_exact = present ? min(max(__builtin_amdgcn_readfirstlane(a.n_exact[route_row]), 0), nKB) : 0;
+    h = lane_half;
+  }
+
   __device__ __forceinline__ int steps() const { return n_exact * sub; }
 
   __device__ __forceinline__ int first_key(int step) const {
@@ -44,7 +64,7 @@ struct ExactPolicy {
   }
 
   // keys past Sk exist only in the final partial block
-  __device__ __forceinline__ void mask(int step, f32x16 (&s)[2][QB], int lane) const {
+  __device__ __forceinline__ void mask(int step, f32x16 (&s)[2][QB], int) const {
     const int k0 = first_key(step);
     if (k0 + kKeysPerTile <= Sk) return;
     const int lim = Sk - k0 - 4 * h;
@@ -68,6 +88,16 @@ struct SummaryPolicy {
   static constexpr bool kFilter = false, kWeighted = true;
   const uint32_t* keep;  // proxy_keep words of this query block
   int Bk, nKB, Wd, last_len, h;
+
+  __device__ __forceinline__ void init(const ProxyArgs& a, int64_t route_row, int nKB_,
+                                       int lane_half) {
+    Bk = a.g.block_k;
+    nKB = nKB_;
+    Wd = (nKB + 31) / 32;
+    keep = a.proxy_keep + route_row * Wd;
+    last_len = a.g.Sk - (nKB - 1) * Bk;
+    h = lane_half;
+  }
 
   __device__ __forceinline__ bool weighted(int) const { return true; }
 
@@ -98,6 +128,27 @@ struct SummaryPolicy {
   }
 };
 
+// Normalise and store this wave's rows of O and their natural-log LSE.
+template <int D, int QB>
+__device__ __forceinline__ void store_rows(const ProxyArgs& a, int b, int hq, int wrow0,
+                                           const f32x16 (&o)[D / 32][QB], const float (&mref)[QB],
+                                           const float (&l)[QB], int lane) {
+  const AttnGeom& g = a.g;
+  const int h = lane >> 5, r32 = lane & 31;
+  float inv[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = half_sum(l[qb]);
+    inv[qb] = lt > 0.f ? 1.f / lt : 0.f;
+    const int row = wrow0 + qb * 32 + r32;
+    if (a.lse != nullptr && h == 0 && row < g.Sq)
+      a.lse[((int64_t)b * g.Hq + hq) * g.Sq + row] =
+          lt > 0.f ? (mref[qb] + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
+  }
+  __bf16* op = (__bf16*)g.o + b * g.os[0] + (int64_t)wrow0 * g.os[1] + hq * g.os[2];
+  store_o<D, QB>(op, g.os[1], g.Sq - wrow0, o, inv, lane);
+}
+
 template <int D, int NW, int QB>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<QB>)))
 void proxy_kernel(ProxyArgs a) {
@@ -108,11 +159,10 @@ void proxy_kernel(ProxyArgs a) {
   const AttnGeom& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 5, r32 = lane & 31;
+  const int h = lane >> 5;
   const int Bk = g.block_k;
   const int nQB = (g.Sq + BR - 1) / BR;
   const int nKB = (g.Sk + Bk - 1) / Bk;
-  const int Wd = (nKB + 31) / 32;
   const int G = g.Hq / g.Hkv;
   const int total = g.B * g.Hq * nQB;
 
@@ -134,19 +184,7 @@ void proxy_kernel(ProxyArgs a) {
   load_q_frags<D, QB>(qf, qsrc, g.qs[1], wrow0, lane);
 
   ExactPolicy<D, NW, QB> pol;
-  pol.kslab = (const __bf16*)g.k + b * g.ks[0] + hk * g.ks[2];
-  pol.vslab = (const __bf16*)g.v + b * g.vs[0] + hk * g.vs[2];
-  pol.exact = a.exact_idx + route_row * nKB;
-  pol.k_stride_b = (int)(g.ks[1] * 2);
-  pol.v_stride_b = (int)(g.vs[1] * 2);
-  pol.k_bytes = (int)(((int64_t)(g.Sk - 1) * g.ks[1] + D) * 2);
-  pol.v_bytes = (int)(((int64_t)(g.Sk - 1) * g.vs[1] + D) * 2);
-  pol.Sk = g.Sk;
-  pol.Bk = Bk;
-  pol.sub = Bk / kKeysPerTile;
-  // never index past the route row, whatever the caller passed
-  pol.n_exact = min(max(__builtin_amdgcn_readfirstlane(a.n_exact[route_row]), 0), nKB);
-  pol.h = h;
+  pol.init(a, b, hk, route_row, nKB, h);
 
   f32x16 o[D / 32][QB];
   float mref[QB], l[QB];
@@ -162,12 +200,7 @@ void proxy_kernel(ProxyArgs a) {
   // proxy tiles: summaries as keys, one tile at a time
   if (a.use_proxy) {
     SummaryPolicy<QB> sp;
-    sp.keep = a.proxy_keep + route_row * Wd;
-    sp.Bk = Bk;
-    sp.nKB = nKB;
-    sp.Wd = Wd;
-    sp.last_len = g.Sk - (nKB - 1) * Bk;
-    sp.h = h;
+    sp.init(a, route_row, nKB, h);
     const int64_t sbase = ((int64_t)b * g.Hkv + hk) * nKB * D;
     const __bf16* kmean = (const __bf16*)a.k_mean + sbase;
     const __bf16* vsum = (const __bf16*)a.v_sum + sbase;
@@ -192,18 +225,7 @@ void proxy_kernel(ProxyArgs a) {
     }
   }
 
-  float inv[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = half_sum(l[qb]);
-    inv[qb] = lt > 0.f ? 1.f / lt : 0.f;
-    const int row = wrow0 + qb * 32 + r32;
-    if (a.lse != nullptr && h == 0 && row < g.Sq)
-      a.lse[((int64_t)b * g.Hq + hq) * g.Sq + row] =
-          lt > 0.f ? (mref[qb] + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
-  }
-  __bf16* op = (__bf16*)g.o + b * g.os[0] + (int64_t)wrow0 * g.os[1] + hq * g.os[2];
-  store_o<D, QB>(op, g.os[1], g.Sq - wrow0, o, inv, lane);
+  store_rows<D, QB>(a, b, hq, wrow0, o, mref, l, lane);
 }
 
 // ---- 64-row query blocks: copy waves and compute waves ------------------------------------------
@@ -243,12 +265,11 @@ void proxy_pc_kernel(ProxyArgs a) {
   const int cw = copier ? wave - kPcGroups * kPcWaves : wave;
   const int grp = cw / kPcWaves, rank = cw % kPcWaves;
   Smem<D, kPcWaves>& sm = sms[grp];
-  const int h = lane >> 5, r32 = lane & 31;
+  const int h = lane >> 5;
   const int Bk = g.block_k;
   const int nQB = (g.Sq + BR - 1) / BR;
   const int nPair = (nQB + kPcGroups - 1) / kPcGroups;
   const int nKB = (g.Sk + Bk - 1) / Bk;
-  const int Wd = (nKB + 31) / 32;
   const int G = g.Hq / g.Hkv;
   const int total = g.B * g.Hq * nPair;
 
@@ -268,19 +289,7 @@ void proxy_pc_kernel(ProxyArgs a) {
   const int64_t route_row = ((int64_t)b * g.Hkv + hk) * nQB + min(qblk, nQB - 1);
 
   ExactPolicy<D, kPcWaves, QB> pol;
-  pol.kslab = (const __bf16*)g.k + b * g.ks[0] + hk * g.ks[2];
-  pol.vslab = (const __bf16*)g.v + b * g.vs[0] + hk * g.vs[2];
-  pol.exact = a.exact_idx + route_row * nKB;
-  pol.k_stride_b = (int)(g.ks[1] * 2);
-  pol.v_stride_b = (int)(g.vs[1] * 2);
-  pol.k_bytes = (int)(((int64_t)(g.Sk - 1) * g.ks[1] + D) * 2);
-  pol.v_bytes = (int)(((int64_t)(g.Sk - 1) * g.vs[1] + D) * 2);
-  pol.Sk = g.Sk;
-  pol.Bk = Bk;
-  pol.sub = Bk / kKeysPerTile;
-  // never index past the route row, whatever the caller passed
-  pol.n_exact = present ? min(max(__builtin_amdgcn_readfirstlane(a.n_exact[route_row]), 0), nKB) : 0;
-  pol.h = h;
+  pol.init(a, b, hk, route_row, nKB, h, present);
   const int n = pol.steps();
   // steps of the other query block of the pair (both walk max(n, n_other) barriers)
   int n_other = 0;
@@ -383,12 +392,7 @@ void proxy_pc_kernel(ProxyArgs a) {
 
   if (n_sum > 0) {
     SummaryPolicy<QB> sp;
-    sp.keep = a.proxy_keep + route_row * Wd;
-    sp.Bk = Bk;
-    sp.nKB = nKB;
-    sp.Wd = Wd;
-    sp.last_len = g.Sk - (nKB - 1) * Bk;
-    sp.h = h;
+    sp.init(a, route_row, nKB, h);
     lds_barrier();
     for (int t = 0; t < n_sum; ++t) {
       lds_barrier();   // summary tile t has landed
@@ -403,15 +407,7 @@ void proxy_pc_kernel(ProxyArgs a) {
   }
   if (!present) return;
 
-  const float lt = half_sum(l[0]);
-  float inv[QB];
-  inv[0] = lt > 0.f ? 1.f / lt : 0.f;
-  const int row = wrow0 + r32;
-  if (a.lse != nullptr && h == 0 && row < g.Sq)
-    a.lse[((int64_t)b * g.Hq + hq) * g.Sq + row] =
-        lt > 0.f ? (mref[0] + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
-  __bf16* op = (__bf16*)g.o + b * g.os[0] + (int64_t)wrow0 * g.os[1] + hq * g.os[2];
-  store_o<D, QB>(op, g.os[1], g.Sq - wrow0, o, inv, lane);
+  store_rows<D, QB>(a, b, hq, wrow0, o, mref, l, lane);
 }
 
 template <int D>
