@@ -27,8 +27,13 @@ struct TileUnit {
 };
 
 // Work item order: KV head major, then query tile, then the G query heads sharing the KV head, so
-// that concurrently running workgroups of one XCD read the same K/V tiles.  Causal: the longest
-// rows first.
+// that concurrently running workgroups of one XCD read the same K/V tiles.
+//
+// Causal rows differ in length, so the longest go first.  The items are cut into blocks of hb KV
+// heads (hb = the KV heads in one XCD's share of the items, at least 1), and inside a block the
+// order is query tile (longest first), then KV head, then query head: each XCD then runs its
+// share longest-first, and the workgroups of one head still walk the same K/V tiles together.
+// With one KV head per block this is the plain order above.
 template <int NW, int QB>
 __device__ __forceinline__ TileUnit tile_unit(const AttnGeom& g, int wave) {
   constexpr int BR = NW * 32 * QB;
@@ -36,14 +41,28 @@ __device__ __forceinline__ TileUnit tile_unit(const AttnGeom& g, int wave) {
   u.nQT = (g.Sq + BR - 1) / BR;
   u.nKT = (g.Sk + kKeysPerTile - 1) / kKeysPerTile;
   const int G = g.Hq / g.Hkv;
-  int item = xcd_remap(blockIdx.x, g.B * g.Hq * u.nQT);
-  const int gq = item % G;
-  item /= G;
-  int qt = item % u.nQT;
-  item /= u.nQT;
-  u.hk = item % g.Hkv;
-  u.b = item / g.Hkv;
-  if (g.causal) qt = u.nQT - 1 - qt;
+  const int total = g.B * g.Hq * u.nQT;
+  int item = xcd_remap(blockIdx.x, total);
+  int gq, qt, bh;
+  if (!g.causal) {
+    gq = item % G;
+    item /= G;
+    qt = item % u.nQT;
+    bh = item / u.nQT;
+  } else {
+    const int per = u.nQT * G;   // items of one KV head
+    const int BH = g.B * g.Hkv;
+    const int hb = max(1, min(BH, (total >> 3) / per));
+    const int h0 = item / (hb * per) * hb;   // first KV head of this item's block
+    const int nh = min(hb, BH - h0);          // KV heads in the block
+    const int c = item - h0 * per;            // position inside the block, < nh * per
+    qt = u.nQT - 1 - c / (nh * G);
+    const int r = c % (nh * G);
+    bh = h0 + r / G;
+    gq = r % G;
+  }
+  u.hk = bh % g.Hkv;
+  u.b = bh / g.Hkv;
   u.qt = qt;
   u.hq = u.hk * G + gq;
   u.row0 = qt * BR;

@@ -70,6 +70,7 @@ def test_llm_causal_reduced(n, m):
     (1, 70, 70, 2, 1, 64, False, 64, 0, 0),       # ragged last group and tile, GQA
     (1, 257, 257, 2, 2, 128, True, 128, 3, 5),    # 1-row last tile, odd windows
     (1, 100, 300, 2, 2, 128, False, 64, 7, 0),    # Sq != Sk
+    (1, 300, 300, 31, 31, 64, True, 128, 4, 16),  # causal work order in blocks of 3 heads (last: 1)
 ])
 def test_edge_shapes(shape, n, m):
     B, Sq, Sk, Hq, Hkv, D, causal, Br, sink, recent = shape

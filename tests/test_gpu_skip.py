@@ -107,6 +107,9 @@ def test_llm_causal_gqa_reduced(lam):
     (1, 192, 192, 2, 2, 128, True, 64),      # D 128 with Br 64
     (1, 1, 1, 1, 1, 128, True, 128),         # single token
     (1, 65, 64, 3, 3, 64, False, 128),       # D 64 with Br 128
+    # causal work order in blocks of several KV heads (longest rows first inside a block):
+    (1, 300, 300, 31, 31, 64, True, 128),    # blocks of 3 heads, the last one holding 1
+    (2, 200, 200, 20, 10, 64, True, 128),    # blocks of 2 KV heads, GQA 2:1
 ])
 @pytest.mark.parametrize("lam", [0.0, 0.9])
 def test_edge_shapes(shape, lam):
