@@ -213,16 +213,21 @@ def run_paths(torch, sa, W, to_dev, steps, warmup):
     _, lam, _ = sa.sa_threshold_from_calib(W.CALIB_A, W.CALIB_B, wl.param("target_sparsity"), S)
     P = tile_pairs(S, S, wl.block_q, wl.block_k, True)
     rec = {"lambda": lam}
-    for name, lm in (("calibrated", lam), ("lambda0", 0.0)):
-        ms = time_steps(torch, lambda: sa.sa_skip_softmax_fwd(
-            qd, kd, vd, o, lm, causal=True, block_q=wl.block_q, block_k=wl.block_k,
-            tile_state=st), steps, warmup)
+    lams = (("calibrated", lam), ("lambda0", 0.0))
+    arms = {name: (lambda lm=lm: sa.sa_skip_softmax_fwd(
+        qd, kd, vd, o, lm, causal=True, block_q=wl.block_q, block_k=wl.block_k,
+        tile_state=st)) for name, lm in lams}
+    times = time_ab(torch, arms, steps, warmup)
+    for name, _ in lams:
+        ms = times[name]
+        arms[name]()
         ts = st.cpu().numpy()
         comp, dense = skip_flops(ts, P, D)
         rec[name] = {"ms": round(ms, 4), "computed_tflops": round(comp / ms / 1e9, 2),
                      "dense_equiv_tflops": round(dense / ms / 1e9, 2),
                      "tile_sparsity": round(float((ts == 1).sum() / max(1, (ts != 2).sum())), 4)}
     rec["speedup_vs_lambda0"] = round(rec["lambda0"]["ms"] / rec["calibrated"]["ms"], 3)
+    rec["timing"] = "median of 5 balanced interleaved rounds per arm"
     out[wl.name] = rec
     del qd, kd, vd, o, st
 
@@ -235,12 +240,14 @@ def run_paths(torch, sa, W, to_dev, steps, warmup):
     dense = 4 * D * tile_pairs(S, S, wl.block_q, wl.block_k, True).sum() * B * H
     rec = {}
     try:
-        for n, m in ((2, 4), (4, 4), (1, 4), (3, 4), (1, 8), (4, 8), (7, 8)):
-            ms = time_steps(torch, lambda: sa.sa_nm_softmax_fwd(
-                qd, kd, vd, o, n, m, wl.param("sink"), wl.param("recent"), causal=True,
-                block_q=wl.block_q, block_k=wl.block_k), steps, warmup)
-            rec[f"{n}:{m}"] = {"ms": round(ms, 4), "dense_equiv_tflops": round(dense / ms / 1e9, 2)}
+        arms = {f"{n}:{m}": (lambda n=n, m=m: sa.sa_nm_softmax_fwd(
+            qd, kd, vd, o, n, m, wl.param("sink"), wl.param("recent"), causal=True,
+            block_q=wl.block_q, block_k=wl.block_k))
+            for n, m in ((2, 4), (4, 4), (1, 4), (3, 4), (1, 8), (4, 8), (7, 8))}
+        for name, ms in time_ab(torch, arms, steps, warmup).items():
+            rec[name] = {"ms": round(ms, 4), "dense_equiv_tflops": round(dense / ms / 1e9, 2)}
         rec["overhead_2:4_vs_4:4"] = round(rec["2:4"]["ms"] / rec["4:4"]["ms"] - 1, 4)
+        rec["timing"] = "median of 5 balanced interleaved rounds per arm"
     except sa.SaError as e:
         rec = {"unavailable": str(e)}
     out[wl.name] = rec
@@ -251,10 +258,14 @@ def run_paths(torch, sa, W, to_dev, steps, warmup):
     _, lam, _ = sa.sa_threshold_from_calib(W.CALIB_A, W.CALIB_B, 0.5, S)
     P = tile_pairs(S, S, wl.block_q, wl.block_k, True)
     rec = {"n:m": "2:4", "lambda": lam}
-    for name, lm in (("calibrated", lam), ("lambda0", 0.0)):
-        ms = time_steps(torch, lambda: sa.sa_skip_nm_softmax_fwd(
-            qd, kd, vd, o, lm, 2, 4, wl.param("sink"), wl.param("recent"), causal=True,
-            block_q=wl.block_q, block_k=wl.block_k, tile_state=st), steps, warmup)
+    lams = (("calibrated", lam), ("lambda0", 0.0))
+    arms = {name: (lambda lm=lm: sa.sa_skip_nm_softmax_fwd(
+        qd, kd, vd, o, lm, 2, 4, wl.param("sink"), wl.param("recent"), causal=True,
+        block_q=wl.block_q, block_k=wl.block_k, tile_state=st)) for name, lm in lams}
+    times = time_ab(torch, arms, steps, warmup)
+    for name, _ in lams:
+        ms = times[name]
+        arms[name]()
         ts = st.cpu().numpy()
         comp, dense_eq = skip_flops(ts, P, D)
         rec[name] = {"ms": round(ms, 4), "computed_tflops": round(comp / ms / 1e9, 2),
@@ -263,6 +274,7 @@ def run_paths(torch, sa, W, to_dev, steps, warmup):
     rec["speedup_vs_lambda0"] = round(rec["lambda0"]["ms"] / rec["calibrated"]["ms"], 3)
     if "2:4" in out[wl.name]:
         rec["speedup_vs_nm_2:4"] = round(out[wl.name]["2:4"]["ms"] / rec["calibrated"]["ms"], 3)
+    rec["timing"] = "median of 5 balanced interleaved rounds per arm"
     out["llm_prefill_skip_nm_s4096"] = rec
     del qd, kd, vd, o, st
 
