@@ -284,8 +284,8 @@ def run_paths(torch, sa, W, to_dev, steps, warmup):
     except sa.SaError as e:
         out["llm_decode_gqa_kv8192"] = {"unavailable": str(e)}
 
-    # proxy-compensated block-sparse attention with bitmask routes, at the survey's workload and at
-    # the shape of the pages' B200 A/B (context)
+    # proxy-compensated block-sparse attention with bitmask routes: 128-token blocks at 25 % exact
+    # (S 16257, partial last block), and the shape of the pages' B200 A/B (context)
     for name in ("proxy_bitmask_s16257", "proxy_page_s32760"):
         out[name] = proxy_leg(torch, sa, W, to_dev, W.WORKLOADS[name], steps, warmup)
     out["proxy_page_s32760"]["context_b200_pages"] = {
