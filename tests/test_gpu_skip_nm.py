@@ -98,6 +98,7 @@ def test_llm_causal_gqa(n, m, lam):
     (2, 130, 130, 4, 1, 128, True, 128),     # 2-row last tile, GQA 4:1
     (1, 257, 257, 2, 2, 64, True, 64),       # D 64, Br 64, 1-row last tile
     (1, 1, 1, 1, 1, 128, True, 128),         # single token
+    (2, 200, 200, 20, 10, 64, True, 128),    # causal work order in blocks of 2 KV heads, GQA 2:1
 ])
 @pytest.mark.parametrize("n,m", [(2, 4), (5, 8)])
 def test_edge_shapes(shape, n, m):
