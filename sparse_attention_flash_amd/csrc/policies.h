@@ -370,10 +370,12 @@ struct NmFilter {
   }
 
   // Threshold pass (M = 8): the group's other four keys are the same elements of lane ^ 32.  Each
-  // lane sorts its four, exchanges the sorted four with lane ^ 32 and takes the N-th and (N+1)-th
-  // largest of the eight; then as for M = 4 (both lanes of a group find the same t and u).
+  // lane sorts its four; one v_permlane32_swap per sorted value then gives every lane both the
+  // lower half's and the upper half's value, and the N-th and (N+1)-th largest of the eight are
+  // read from those two sorted lists (the K-th largest of a union does not depend on which list
+  // is which, so both lanes of a group find the same t and u); then as for M = 4.
   template <int N>
-  static __device__ __forceinline__ void threshold_apply8(f32x16 (&s)[2][QB], int lane, bool& tie) {
+  static __device__ __forceinline__ void threshold_apply8(f32x16 (&s)[2][QB], bool& tie) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -381,11 +383,16 @@ struct NmFilter {
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
           f32x16& v = s[kb][qb];
-          float a[4], b[4];
+          float a[4], lo[4], hi[4];
           sort4_desc(v[4 * gi], v[4 * gi + 1], v[4 * gi + 2], v[4 * gi + 3], a);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) b[e] = other_half(a[e], lane);
-          const float t = kth_largest8<N>(a, b), u = kth_largest8<N + 1>(a, b);
+          for (int e = 0; e < 4; ++e) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[e]),
+                                                             __float_as_uint(a[e]), false, false);
+            lo[e] = __uint_as_float(sw[0]);   // the value of lane l & 31
+            hi[e] = __uint_as_float(sw[1]);   // the value of lane l | 32
+          }
+          const float t = kth_largest8<N>(lo, hi), u = kth_largest8<N + 1>(lo, hi);
           tie = tie || (u == t && t != -INFINITY);
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[4 * gi + e] = v[4 * gi + e] < t ? -INFINITY : v[4 * gi + e];
@@ -433,13 +440,13 @@ struct NmFilter {
         else if (n == 3) threshold_apply<3>(s, tie);
       } else {
         switch (n) {
-          case 1: threshold_apply8<1>(s, lane, tie); break;
-          case 2: threshold_apply8<2>(s, lane, tie); break;
-          case 3: threshold_apply8<3>(s, lane, tie); break;
-          case 4: threshold_apply8<4>(s, lane, tie); break;
-          case 5: threshold_apply8<5>(s, lane, tie); break;
-          case 6: threshold_apply8<6>(s, lane, tie); break;
-          case 7: threshold_apply8<7>(s, lane, tie); break;
+          case 1: threshold_apply8<1>(s, tie); break;
+          case 2: threshold_apply8<2>(s, tie); break;
+          case 3: threshold_apply8<3>(s, tie); break;
+          case 4: threshold_apply8<4>(s, tie); break;
+          case 5: threshold_apply8<5>(s, tie); break;
+          case 6: threshold_apply8<6>(s, tie); break;
+          case 7: threshold_apply8<7>(s, tie); break;
           default: break;
         }
       }
