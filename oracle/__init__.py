@@ -12,6 +12,8 @@ Each wrapper returns results in natural layouts:
 * ``nm_softmax``: ``o``, ``lse``, ``keep_bits [B,Hq,Sq,ceil(Sk/32)]`` (uint32, LSB first).
 * ``skip_nm_softmax``: ``o``, ``lse``, ``tile_state``, ``rowmax`` as skip_softmax, plus
   ``keep_bits`` as nm_softmax.
+* ``skip_replay``: ``tile_state`` alone, replayed from given fp32 tile maxima (no dot products).
+* ``nm_keep_replay``: N:M keep bits alone, replayed from given fp32 scores (no dot products).
 * ``route_prep``: ``n_exact``, ``exact_idx`` (ascending, -1 padded), ``proxy_keep``.
 * ``bsr_route_prep``: the same triple from BSR rows, plus the count of non-canonical rows.
 * ``proxy_fwd``: ``o``, ``lse``.
@@ -65,6 +67,10 @@ def _load():
         lib.oracle_skip_nm_softmax.argtypes = ([I] * 9 + [D, D] + [I] * 4 + [P, P, P, I] +
                                                [P] * 5 + [I64] + [P] * 5)
         lib.oracle_skip_nm_softmax.restype = I
+        lib.oracle_skip_replay.argtypes = [I] * 7 + [D, P, I64, P, P]
+        lib.oracle_skip_replay.restype = I
+        lib.oracle_nm_keep_replay.argtypes = [I] * 7 + [P, I64, P, P]
+        lib.oracle_nm_keep_replay.restype = I
         lib.oracle_route_prep.argtypes = [I64, I, P, P, P, P]
         lib.oracle_route_prep.restype = I
         lib.oracle_bsr_route_prep.argtypes = [I64, I, P, I64, P, P, P, P, P]
@@ -198,6 +204,40 @@ def skip_nm_softmax(q, k, v, *, causal, block_q, block_k, scale, lam, n, m, sink
     kb = kb.reshape(B, Hq, nQT * block_q, W)[:, :, :Sq]
     return (np.ascontiguousarray(o), np.ascontiguousarray(lse), st.reshape(B, Hq, nQT, nKT),
             rm.reshape(B, Hq, nQT, nKT, block_q), np.ascontiguousarray(kb))
+
+
+def skip_replay(rowmax, *, batch, heads_q, seqlen_q, seqlen_k, causal, block_q, block_k, lam,
+                units=None):
+    """Skip decisions alone, replayed from fp32 tile maxima (no attention arithmetic).
+
+    ``rowmax`` holds the listed units' maxima, ``[n_units, nKT, block_q]`` float32 (all units in
+    order when ``units`` is None); returns ``tile_state [n_units, nKT]`` (0 kept, 1 skipped,
+    2 not visited)."""
+    nQT, nKT = -(-seqlen_q // block_q), -(-seqlen_k // block_k)
+    u, n = _units(units, batch * heads_q * nQT)
+    rm = np.ascontiguousarray(rowmax, dtype=np.float32)
+    assert rm.size == n * nKT * block_q, (rm.shape, n, nKT, block_q)
+    st = np.zeros((n, nKT), np.uint8)
+    rc = _load().oracle_skip_replay(batch, heads_q, seqlen_q, seqlen_k, int(causal), block_q,
+                                    block_k, float(lam), _ptr(u), n, _ptr(rm), _ptr(st))
+    if rc:
+        raise ValueError("oracle_skip_replay rejected its arguments")
+    return st
+
+
+def nm_keep_replay(scores, row_pos, *, seqlen_q, causal, n, m, sink, recent):
+    """N:M keep bits alone, replayed from fp32 score rows ``[n_rows, Sk]`` whose query positions
+    are ``row_pos``; returns ``keep [n_rows, ceil(Sk/32)]`` uint32 (LSB first)."""
+    sc = np.ascontiguousarray(scores, dtype=np.float32)
+    rp = np.ascontiguousarray(np.asarray(row_pos, dtype=np.int32)).ravel()
+    n_rows, Sk = sc.shape
+    assert rp.size == n_rows
+    keep = np.zeros((n_rows, -(-Sk // 32)), np.uint32)
+    rc = _load().oracle_nm_keep_replay(int(seqlen_q), Sk, int(causal), int(n), int(m), int(sink),
+                                       int(recent), _ptr(rp), n_rows, _ptr(sc), _ptr(keep))
+    if rc:
+        raise ValueError("oracle_nm_keep_replay rejected its arguments")
+    return keep
 
 
 def route_prep(bitmask, n_kv_blocks):

@@ -195,6 +195,58 @@ int oracle_skip_softmax(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causa
     return bad;
 }
 
+/* ------------------------------------------------------------------------------------------------
+ * Skip-softmax decisions replayed from given tile maxima, without the attention arithmetic.
+ * [MO-diff] introduction + "Threshold Modes".  This is the decision chain of oracle_skip_softmax in
+ * mode 1 on its own (no logits, no softmax), so that a whole full-size run can be replayed:
+ *
+ *   for each unit (b, hq, query tile i of Br rows; valid rows r0 .. r1-1) and each key tile j of Bc
+ *   keys in ascending order, visited when it holds an unmasked pair (causal: j*Bc <= r1-1):
+ *     skip(j) = every valid row rr has  M_j[rr] < (float)(m32[rr] + L32),
+ *               L32 = (float)log2((double)(float)lambda), -inf for lambda == 0;
+ *     a kept tile raises m32[rr] to max(m32[rr], M_j[rr]); a skipped tile changes nothing.
+ *
+ * The comparison and the running max are fp32, as in mode 1 of oracle_skip_softmax.
+ * rowmax holds the maxima of the listed units only, compact: [n_units][nKT][Br] (fp32, log2
+ * domain; entries of rows >= Sq and of unvisited tiles are not read).  state_out [n_units][nKT]:
+ * 0 kept, 1 skipped, 2 not visited.  Units are linear (b*Hq + hq)*nQT + i; NULL means all.
+ * ----------------------------------------------------------------------------------------------*/
+int oracle_skip_replay(int B, int Hq, int Sq, int Sk, int causal, int Br, int Bc, double lambda,
+                       const int64_t* units, int64_t n_units, const float* rowmax,
+                       uint8_t* state_out) {
+    if (B < 1 || Hq < 1 || Sq < 1 || Sk < 1 || Br < 1 || Bc < 1) return 1;
+    if (causal && Sq != Sk) return 1;
+    if (!(lambda >= 0.0) || isinf(lambda)) return 1;
+    const int nQT = (Sq + Br - 1) / Br, nKT = (Sk + Bc - 1) / Bc;
+    const float L32 = (lambda == 0.0) ? -INFINITY : (float)log2((double)(float)lambda);
+    int bad = 0;
+
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t u = 0; u < n_units; ++u) {
+        const int64_t unit = units ? units[u] : u;
+        if (unit < 0 || unit >= (int64_t)B * Hq * nQT) { bad = 1; continue; }
+        const int i = (int)(unit % nQT);
+        const int r0 = i * Br, r1 = (r0 + Br < Sq) ? r0 + Br : Sq, nr = r1 - r0;
+        float* m32 = malloc(sizeof(float) * Br);
+        for (int rr = 0; rr < Br; ++rr) m32[rr] = -INFINITY;
+        for (int j = 0; j < nKT; ++j) {
+            uint8_t* st = &state_out[u * nKT + j];
+            const int visited = causal ? (j * Bc <= r1 - 1) : 1;
+            if (!visited) { *st = 2; continue; }
+            const float* Min = &rowmax[((size_t)u * nKT + j) * Br];
+            int skip = 1;
+            for (int rr = 0; rr < nr; ++rr)
+                if (!(Min[rr] < (float)(m32[rr] + L32))) { skip = 0; break; }
+            *st = (uint8_t)skip;
+            if (skip) continue;
+            for (int rr = 0; rr < nr; ++rr)
+                if (Min[rr] > m32[rr]) m32[rr] = Min[rr];
+        }
+        free(m32);
+    }
+    return bad;
+}
+
 /* N:M keep flags of one query row r over all Sk keys (the definition below, under oracle_nm_softmax):
  * x[kk] holds the ranking scores (-inf where not allowed); keep[kk] receives allowed and (dense or
  * rank < N). */
@@ -307,6 +359,48 @@ int oracle_nm_softmax(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
             lse_out[u * Br + rr] = mu + log(den);
         }
         free(x); free(keep); free(num);
+    }
+    return bad;
+}
+
+/* ------------------------------------------------------------------------------------------------
+ * N:M keep bits replayed from given scores, without the attention arithmetic.  [MO-llm] "N:M
+ * Sparse Softmax": the keep rule of oracle_nm_softmax (its definition, nm_keep_row) applied to
+ * score rows taken as given, as mode 1 of oracle_nm_softmax does, with no output computed.
+ *
+ *   row_pos[i]   the query position r of score row i (0 <= r < Sq)
+ *   scores       [n_rows][Sk] fp32 raw scores q.k (entries of masked keys are not read: a key
+ *                with causal && k > r is -inf)
+ *   keep_out     [n_rows][W], W = ceil(Sk/32): bit k&31 of word k>>5 (LSB first); padding 0.
+ * ----------------------------------------------------------------------------------------------*/
+int oracle_nm_keep_replay(int Sq, int Sk, int causal, int N, int Mg, int sink, int recent,
+                          const int32_t* row_pos, int64_t n_rows, const float* scores,
+                          uint32_t* keep_out) {
+    if (Sq < 1 || Sk < 1 || Mg < 1 || N < 1 || N > Mg || sink < 0 || recent < 0) return 1;
+    if (causal && Sq != Sk) return 1;
+    const int W = (Sk + 31) / 32;
+    int bad = 0;
+
+#pragma omp parallel
+    {
+        double* x = malloc(sizeof(double) * Sk);
+        unsigned char* keep = malloc(Sk);
+#pragma omp for schedule(dynamic, 64)
+        for (int64_t i = 0; i < n_rows; ++i) {
+            const int r = row_pos[i];
+            uint32_t* kw = &keep_out[i * W];
+            for (int w = 0; w < W; ++w) kw[w] = 0u;
+            if (r < 0 || r >= Sq) { bad = 1; continue; }
+            for (int kk = 0; kk < Sk; ++kk) {
+                const int allowed = !causal || kk <= r;
+                x[kk] = allowed ? (double)scores[i * Sk + kk] : -INFINITY;
+            }
+            nm_keep_row(r, Sk, causal, N, Mg, sink, recent, x, keep);
+            for (int kk = 0; kk < Sk; ++kk)
+                if (keep[kk]) kw[kk >> 5] |= 1u << (kk & 31);
+        }
+        free(x);
+        free(keep);
     }
     return bad;
 }

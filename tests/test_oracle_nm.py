@@ -148,3 +148,43 @@ def test_rejects_bad_arguments():
             _run(q, k, v, False, n, m)
     with pytest.raises(ValueError):
         _run(q, k, v, False, 1, 4, sink=-1)
+
+
+# ---- keep bits alone, replayed from given scores (oracle.nm_keep_replay) ------------------------
+
+@pytest.mark.parametrize("n,m", NM_PAIRS + [(4, 4), (8, 8)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_keep_replay_matches_argsort(n, m, causal):
+    """Keep bits from fp32 scores equal a numpy stable-argsort top-n over the same scores."""
+    Sq, Hq, D, sink, recent = 150, 2, 32, 3, 9
+    q, k, _ = W.gen_llm(41, 1, Sq, Hq, Hq, D)
+    s32 = refs.scores(q, k).astype(np.float32)[0]               # [H, Sq, Sk]
+    allowed = np.tril(np.ones((Sq, Sq), bool)) if causal else np.ones((Sq, Sq), bool)
+    rows = s32.reshape(Hq * Sq, Sq)
+    pos = np.tile(np.arange(Sq), Hq)
+    got = oracle.nm_keep_replay(rows, pos, seqlen_q=Sq, causal=causal, n=n, m=m, sink=sink,
+                                recent=recent)
+    s = np.where(allowed[None], s32.astype(np.float64), -np.inf)
+    keep = np.zeros_like(s, dtype=bool)
+    for g0 in range(0, Sq, m):
+        g1 = min(Sq, g0 + m)
+        order = np.argsort(-s[..., g0:g1], axis=-1, kind="stable")
+        top = np.zeros(order.shape, bool)
+        np.put_along_axis(top, order[..., :n], True, axis=-1)
+        keep[..., g0:g1] = top
+    r = np.arange(Sq)[:, None]
+    kk = np.arange(Sq)[None, :]
+    keep = (keep | (kk < sink) | ((r - kk >= 0) & (r - kk < recent))) & allowed
+    mask = _bits_to_mask(got.reshape(1, Hq, Sq, -1), Sq)[0]
+    assert np.array_equal(mask, keep)
+
+
+def test_keep_replay_equals_full_oracle_replay():
+    Sq, H, D = 200, 2, 32
+    q, k, v = W.gen_llm(42, 1, Sq, H, H, D)
+    s32 = refs.scores(q, k).astype(np.float32)
+    for n, m in ((2, 4), (5, 8)):
+        _, _, kb = _run(q, k, v, True, n, m, 4, 16, mode=1, scores_in=s32)
+        got = oracle.nm_keep_replay(s32.reshape(H * Sq, Sq), np.tile(np.arange(Sq), H),
+                                    seqlen_q=Sq, causal=True, n=n, m=m, sink=4, recent=16)
+        assert np.array_equal(got, kb.reshape(H * Sq, -1))

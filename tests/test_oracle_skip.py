@@ -248,3 +248,83 @@ def test_rejects_bad_arguments():
         _run(q, k, v, False, 64, 64, float("nan"))
     with pytest.raises(ValueError):
         _run(q, k[:, :32], v[:, :32], True, 64, 64, 0.1)   # causal needs Sq == Sk
+
+
+# ---- decisions-only replay (oracle.skip_replay) -------------------------------------------------
+
+def _fp32_closed_form_states(rm32, Sq, Br, Bc, causal, lam):
+    """For lambda <= 1: a skipped tile has M < fl32(m + L) <= m, so it never raises the running
+    max and m is the fp32 prefix max of every earlier visited tile; keep(j) holds exactly when
+    some valid row has M_j >= fl32(prefix + L32).  Vectorised numpy over [units, nKT, Br]."""
+    n, nKT, _ = rm32.shape
+    L32 = np.float32(math.log2(np.float64(np.float32(lam))))
+    st = np.zeros((n, nKT), np.uint8)
+    qt = np.arange(n) % (-(-Sq // Br))
+    nr = np.minimum(Br, Sq - qt * Br)
+    valid = np.arange(Br)[None, :] < nr[:, None]
+    prefix = np.full((n, Br), -np.inf, np.float32)
+    for j in range(nKT):
+        visited = (j * Bc <= qt * Br + nr - 1) if causal else np.ones(n, bool)
+        M = rm32[:, j, :]
+        keep = ((M >= (prefix + L32)) & valid).any(axis=1)
+        st[:, j] = np.where(visited, np.where(keep, 0, 1), 2)
+        prefix = np.where(visited[:, None], np.maximum(prefix, M), prefix)
+    return st
+
+
+@pytest.mark.parametrize("lam", [0.1, 0.4, 0.8, 1.0])
+@pytest.mark.parametrize("causal,Sq,Br,Bc", [(True, 512, 128, 64), (False, 300, 64, 64),
+                                             (True, 200, 32, 128), (False, 257, 32, 64)])
+def test_skip_replay_matches_fp32_closed_form(lam, causal, Sq, Br, Bc):
+    """Replay from maxima of numpy fp32 logits equals the fp32 closed form (lambda <= 1)."""
+    D, H = 64, 3
+    q, k, _ = W.gen_llm(31, 1, Sq, H, H, D)
+    c = (1 / math.sqrt(D)) * math.log2(math.e)
+    t = (c * refs.scores(q, k)).astype(np.float32)[0]          # [H, Sq, Sk]
+    if causal:
+        t = np.where(np.tril(np.ones((Sq, Sq), bool)), t, -np.inf).astype(np.float32)
+    nQT, nKT = -(-Sq // Br), -(-Sq // Bc)
+    rm = np.full((H, nQT, nKT, Br), -np.inf, np.float32)
+    for i in range(nQT):
+        for j in range(nKT):
+            blk = t[:, i * Br:(i + 1) * Br, j * Bc:(j + 1) * Bc]
+            rm[:, i, j, :blk.shape[1]] = blk.max(axis=-1)
+    rm = rm.reshape(H * nQT, nKT, Br)
+    st = oracle.skip_replay(rm, batch=1, heads_q=H, seqlen_q=Sq, seqlen_k=Sq, causal=causal,
+                            block_q=Br, block_k=Bc, lam=lam)
+    ref = _fp32_closed_form_states(rm, Sq, Br, Bc, causal, lam)
+    assert np.array_equal(st, ref)
+    vis = st != 2
+    if (causal, Sq, Br, Bc) == (False, 257, 32, 64):   # not vacuous: this case skips 22-67 tiles
+        assert (st[vis] == 1).sum() >= 20
+
+
+@pytest.mark.parametrize("lam,state", [(0.0, [0, 0, 0, 0]), (2.0, [0, 0, 1, 0]),
+                                       (4.0, [0, 0, 1, 1]), (8.0, [0, 1, 1, 0])])
+def test_skip_replay_hand_built_sequence(lam, state):
+    """Maxima [0, 2, 1, 3.5] of one row over four one-key tiles: the strict test and the
+    untouched running max on a skip (lambda > 1), as in the hand-built oracle case above."""
+    rm = np.array([[[0.0], [2.0], [1.0], [3.5]]], np.float32)
+    st = oracle.skip_replay(rm, batch=1, heads_q=1, seqlen_q=1, seqlen_k=4, causal=False,
+                            block_q=1, block_k=1, lam=lam)
+    assert st[0].tolist() == state
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.5, 1.0, 1.5, 3.0, 1e30])
+@pytest.mark.parametrize("case", CASES)
+def test_skip_replay_equals_full_oracle_replay(case, lam):
+    """On any maxima, the decisions-only replay equals mode 1 of the full oracle."""
+    B, Sq, Sk, Hq, Hkv, D, causal, Br, Bc = case
+    q, k, v = W.gen_llm(32, B, Sq, Hq, Hkv, D) if Sq == Sk else W.gen_iid(32, B, Sq, Sk, Hq, Hkv, D)
+    _, _, _, rm = _run(q, k, v, causal, Br, Bc, 0.0)
+    rm32 = rm.astype(np.float32)
+    _, _, st_full, _ = _run(q, k, v, causal, Br, Bc, lam, mode=1, rowmax_in=rm32)
+    nQT, nKT = st_full.shape[2:]
+    st = oracle.skip_replay(rm32.reshape(-1, nKT, Br), batch=B, heads_q=Hq, seqlen_q=Sq,
+                            seqlen_k=Sk, causal=causal, block_q=Br, block_k=Bc, lam=lam)
+    assert np.array_equal(st, st_full.reshape(-1, nKT))
+    units = np.array([0, B * Hq * nQT - 1])
+    st_u = oracle.skip_replay(rm32.reshape(-1, nKT, Br)[units], batch=B, heads_q=Hq, seqlen_q=Sq,
+                              seqlen_k=Sk, causal=causal, block_q=Br, block_k=Bc, lam=lam,
+                              units=units)
+    assert np.array_equal(st_u, st_full.reshape(-1, nKT)[units])
