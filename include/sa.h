@@ -227,7 +227,11 @@ sa_status sa_bsr_route_prep(const sa_attn_desc* desc, const int32_t* block_indpt
  *   s = softmax_scale * q.k.   A row with nothing to attend to gets O = 0 and lse = -inf.
  *
  *   k_mean, v_sum   bf16 [B, Hkv, nKB, head_dim], contiguous (caller-provided summaries).
- *   n_exact, exact_idx, proxy_keep   as produced by sa_bitmask_route_prep.
+ *   n_exact, exact_idx, proxy_keep   as produced by sa_bitmask_route_prep.  The kernel reads
+ *                   n_exact clamped to [0, nKB] and the first n_exact entries of the row's
+ *                   exact_idx; an entry outside [0, nKB) (such as the -1 fill after the real
+ *                   entries, read when n_exact exceeds them) contributes nothing and reads no K/V.
+ *                   Entries are otherwise trusted: a repeated block is attended once per entry.
  *   lse             optional, fp32 [B, Hq, Sq].
  * Non-causal only (causal -> SA_ERR_UNSUPPORTED).  Supported: head_dim 128 (and 64),
  * block_q 128 or 64, block_k 64 or 128.

@@ -117,10 +117,41 @@ def _bsh_strides(t, name):
     return (t.stride(0), t.stride(1), t.stride(2))
 
 
+_U8 = (torch.uint8,)
+_U32 = (torch.int32, torch.uint32)
+_F32 = (torch.float32,)
+
+
+def _need(t, name, numel, dtypes):
+    """An optional output or route buffer (None passes): a contiguous tensor of one of ``dtypes``
+    with exactly ``numel`` elements, the size sa.h gives for it."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
+
+
 def make_desc(q, k, v=None, o=None, *, causal=False, block_q=128, block_k=64, scale=None):
-    """sa_attn_desc from tensor shapes/strides (v and o default to the strides of k and q)."""
+    """sa_attn_desc from tensor shapes/strides (v and o default to the strides of k and q).
+
+    Checks that the tensors agree: v has k's shape, o has q's, and q, k share batch and
+    head_dim."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [batch, seq, heads, head_dim]")
     B, Sq, Hq, D = q.shape
     Sk, Hkv = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"k {tuple(k.shape)} does not match q {tuple(q.shape)} in batch/head_dim")
+    if v is not None and v.shape != k.shape:
+        raise ValueError(f"v {tuple(v.shape)} must have k's shape {tuple(k.shape)}")
+    if o is not None and o.shape != q.shape:
+        raise ValueError(f"o {tuple(o.shape)} must have q's shape {tuple(q.shape)}")
     d = sa_attn_desc()
     d.batch, d.heads_q, d.heads_kv, d.seqlen_q, d.seqlen_k, d.head_dim = B, Hq, Hkv, Sq, Sk, D
     d.causal = int(bool(causal))
@@ -135,10 +166,30 @@ def make_desc(q, k, v=None, o=None, *, causal=False, block_q=128, block_k=64, sc
     return d
 
 
+def _skip_outputs(d, rows, tile_state, head_counters, lse, rowmax):
+    """Sizes of the skip-softmax outputs for decision blocks of ``rows`` query rows."""
+    if min(rows, d.block_k, d.seqlen_q, d.seqlen_k) < 1:
+        return   # the library rejects the sizes themselves
+    nR, nKT = -(-d.seqlen_q // rows), -(-d.seqlen_k // d.block_k)
+    BH = d.batch * d.heads_q
+    _need(tile_state, "tile_state", BH * nR * nKT, _U8)
+    _need(head_counters, "head_counters", BH * 2, _U32)
+    _need(lse, "lse", BH * d.seqlen_q, _F32)
+    _need(rowmax, "dbg_tile_rowmax", BH * nR * nKT * rows, _F32)
+
+
+def _nm_outputs(d, lse, keep_bits, scores):
+    BH = d.batch * d.heads_q
+    _need(lse, "lse", BH * d.seqlen_q, _F32)
+    _need(keep_bits, "dbg_keep_bits", BH * d.seqlen_q * (-(-d.seqlen_k // 32)), _U32)
+    _need(scores, "dbg_scores", BH * d.seqlen_q * d.seqlen_k, _F32)
+
+
 def sa_skip_softmax_fwd(q, k, v, o, lam, *, causal=False, block_q=128, block_k=64, scale=None,
                         tile_state=None, head_counters=None, lse=None, dbg_tile_rowmax=None,
                         stream=None):
     d = make_desc(q, k, v, o, causal=causal, block_q=block_q, block_k=block_k, scale=scale)
+    _skip_outputs(d, d.block_q, tile_state, head_counters, lse, dbg_tile_rowmax)
     _check(_lib.sa_skip_softmax_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                     float(lam), _ptr(tile_state), _ptr(head_counters), _ptr(lse),
                                     _ptr(dbg_tile_rowmax), _stream(stream)),
@@ -149,6 +200,7 @@ def sa_nm_softmax_fwd(q, k, v, o, n, m, dense_sink_tokens=0, dense_recent_tokens
                       causal=False, block_q=128, block_k=64, scale=None, lse=None,
                       dbg_keep_bits=None, dbg_scores=None, stream=None):
     d = make_desc(q, k, v, o, causal=causal, block_q=block_q, block_k=block_k, scale=scale)
+    _nm_outputs(d, lse, dbg_keep_bits, dbg_scores)
     _check(_lib.sa_nm_softmax_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), int(n),
                                   int(m), int(dense_sink_tokens), int(dense_recent_tokens),
                                   _ptr(lse), _ptr(dbg_keep_bits), _ptr(dbg_scores),
@@ -161,6 +213,8 @@ def sa_skip_nm_softmax_fwd(q, k, v, o, lam, n, m, dense_sink_tokens=0, dense_rec
                            head_counters=None, lse=None, dbg_tile_rowmax=None, dbg_keep_bits=None,
                            dbg_scores=None, stream=None):
     d = make_desc(q, k, v, o, causal=causal, block_q=block_q, block_k=block_k, scale=scale)
+    _skip_outputs(d, d.block_q, tile_state, head_counters, None, dbg_tile_rowmax)
+    _nm_outputs(d, lse, dbg_keep_bits, dbg_scores)
     _check(_lib.sa_skip_nm_softmax_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                        float(lam), int(n), int(m), int(dense_sink_tokens),
                                        int(dense_recent_tokens), _ptr(tile_state),
@@ -184,6 +238,14 @@ def sa_skip_softmax_decode_fwd(q, k, v, o, lam, *, block_k=64, seqlens_k=None, n
                                lse=None, dbg_tile_rowmax=None, stream=None):
     """q, o [B, 1, Hq, D]; k, v [B, Sk, Hkv, D].  Without a workspace one is allocated."""
     d = make_desc(q, k, v, o, block_q=64, block_k=block_k, scale=scale)
+    BH, nKT = d.batch * d.heads_q, -(-d.seqlen_k // max(1, d.block_k))
+    _need(seqlens_k, "seqlens_k", d.batch, (torch.int32,))
+    _need(tile_state, "tile_state", BH * nKT, _U8)
+    _need(head_counters, "head_counters", BH * 2, _U32)
+    _need(lse, "lse", BH, _F32)
+    _need(dbg_tile_rowmax, "dbg_tile_rowmax", BH * nKT, _F32)
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     if workspace is None:
         nbytes, _ = sa_skip_softmax_decode_workspace(q, k, lam, block_k=block_k,
                                                      num_splits=num_splits, scale=scale)
@@ -196,15 +258,38 @@ def sa_skip_softmax_decode_fwd(q, k, v, o, lam, *, block_k=64, seqlens_k=None, n
            "sa_skip_softmax_decode_fwd")
 
 
+def _nkb(d):
+    return -(-d.seqlen_k // d.block_k)
+
+
+def _route_rows(d):
+    return d.batch * d.heads_kv * (-(-d.seqlen_q // d.block_q))
+
+
+def _sizes_ok(d):
+    return min(d.batch, d.heads_kv, d.seqlen_q, d.seqlen_k, d.block_q, d.block_k) >= 1
+
+
+def _route_outputs(d, n_exact, exact_idx, proxy_keep):
+    for t, name in ((n_exact, "n_exact"), (exact_idx, "exact_idx"), (proxy_keep, "proxy_keep")):
+        if t is None:
+            raise ValueError(f"{name} is required")
+    if not _sizes_ok(d):
+        return   # the library rejects the sizes themselves
+    rows, nKB = _route_rows(d), _nkb(d)
+    _need(n_exact, "n_exact", rows, _U32)
+    _need(exact_idx, "exact_idx", rows * nKB, _U32)
+    _need(proxy_keep, "proxy_keep", rows * (-(-nKB // 32)), _U32)
+
+
 def sa_bitmask_route_prep(bitmask, n_exact, exact_idx, proxy_keep, *, batch, heads_kv, seqlen_q,
                           seqlen_k, block_q, block_k, stream=None):
     d = sa_attn_desc()
     d.batch, d.heads_kv, d.heads_q = batch, heads_kv, heads_kv
     d.seqlen_q, d.seqlen_k, d.block_q, d.block_k = seqlen_q, seqlen_k, block_q, block_k
-    for t, dt in ((bitmask, torch.int32), (n_exact, torch.int32), (exact_idx, torch.int32),
-                  (proxy_keep, torch.int32)):
-        if t.dtype not in (torch.int32, torch.uint32) or not t.is_contiguous():
-            raise TypeError("route tensors must be contiguous 32-bit integer tensors")
+    _route_outputs(d, n_exact, exact_idx, proxy_keep)
+    if _sizes_ok(d):
+        _need(bitmask, "bitmask", _route_rows(d) * (-(-_nkb(d) // 32)), _U32)
     _check(_lib.sa_bitmask_route_prep(ctypes.byref(d), _ptr(bitmask), _ptr(n_exact),
                                       _ptr(exact_idx), _ptr(proxy_keep), _stream(stream)),
            "sa_bitmask_route_prep")
@@ -215,9 +300,11 @@ def sa_bsr_route_prep(block_indptr, block_indices, n_exact, exact_idx, proxy_kee
     d = sa_attn_desc()
     d.batch, d.heads_kv, d.heads_q = batch, heads_kv, heads_kv
     d.seqlen_q, d.seqlen_k, d.block_q, d.block_k = seqlen_q, seqlen_k, block_q, block_k
-    for t in (block_indptr, block_indices, n_exact, exact_idx, proxy_keep, bad_rows):
-        if t is not None and (t.dtype not in (torch.int32, torch.uint32) or not t.is_contiguous()):
-            raise TypeError("route tensors must be contiguous 32-bit integer tensors")
+    _route_outputs(d, n_exact, exact_idx, proxy_keep)
+    if _sizes_ok(d):
+        _need(block_indptr, "block_indptr", _route_rows(d) + 1, (torch.int32,))
+    _need(block_indices, "block_indices", block_indices.numel(), (torch.int32,))
+    _need(bad_rows, "bad_rows", 1, _U32)
     nnz = block_indices.numel()
     _check(_lib.sa_bsr_route_prep(ctypes.byref(d), _ptr(block_indptr),
                                   _ptr(block_indices) if nnz else None, nnz, _ptr(n_exact),
@@ -229,9 +316,12 @@ def sa_bsr_route_prep(block_indptr, block_indices, n_exact, exact_idx, proxy_kee
 def sa_proxy_block_sparse_fwd(q, k, v, k_mean, v_sum, n_exact, exact_idx, proxy_keep, use_proxy,
                               o, *, block_q=128, block_k=128, scale=None, lse=None, stream=None):
     d = make_desc(q, k, v, o, causal=False, block_q=block_q, block_k=block_k, scale=scale)
-    for t in (k_mean, v_sum):
-        if t is not None and (t.dtype != torch.bfloat16 or not t.is_contiguous()):
-            raise TypeError("k_mean / v_sum must be contiguous bfloat16 [B, Hkv, nKB, D]")
+    if _sizes_ok(d):
+        summ = d.batch * d.heads_kv * _nkb(d) * d.head_dim
+        _need(k_mean, "k_mean", summ, (torch.bfloat16,))
+        _need(v_sum, "v_sum", summ, (torch.bfloat16,))
+    _route_outputs(d, n_exact, exact_idx, proxy_keep)
+    _need(lse, "lse", d.batch * d.heads_q * d.seqlen_q, _F32)
     _check(_lib.sa_proxy_block_sparse_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v),
                                           _ptr(k_mean), _ptr(v_sum), _ptr(n_exact),
                                           _ptr(exact_idx), _ptr(proxy_keep), int(use_proxy),
@@ -253,6 +343,7 @@ def sa_skip_softmax_calibrate(q, k, v, o, trial_lambdas, head_counters, *, causa
                               block_q=128, block_k=64, scale=None, stream=None):
     """Tile sparsity of each trial threshold (a list of floats); blocks until done."""
     d = make_desc(q, k, v, o, causal=causal, block_q=block_q, block_k=block_k, scale=scale)
+    _need(head_counters, "head_counters", d.batch * d.heads_q * 2, _U32)
     trials = (ctypes.c_float * len(trial_lambdas))(*map(float, trial_lambdas))
     out = (ctypes.c_double * len(trial_lambdas))()
     _check(_lib.sa_skip_softmax_calibrate(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o),

@@ -27,7 +27,7 @@ struct ExactPolicy {
   const __bf16* vslab;
   const int32_t* exact;  // ascending exact block indices of this query block
   int k_stride_b, v_stride_b, k_bytes, v_bytes;
-  int Sk, Bk, sub, n_exact, h;
+  int Sk, Bk, sub, n_exact, nKB, h;
 
   // the route row of query block route_row of (b, KV head hk); a row that is not present (the
   // missing half of a 64-row pair) has no steps
@@ -46,13 +46,18 @@ struct ExactPolicy {
     sub = Bk / kKeysPerTile;
     // never index past the route row, whatever the caller passed
     n_exact = present ? min(max(__builtin_amdgcn_readfirstlane(a.n_exact[route_row]), 0), nKB) : 0;
+    this->nKB = nKB;
     h = lane_half;
   }
 
   __device__ __forceinline__ int steps() const { return n_exact * sub; }
 
+  // A block index outside [0, nKB) (the -1 fill after a route's real entries, read when the
+  // caller's n_exact exceeds them, or any other bad value) becomes an empty step: it is placed at
+  // block nKB, past the last key, so its copies read no bytes and mask() drops every key.
   __device__ __forceinline__ int first_key(int step) const {
-    const int blk = __builtin_amdgcn_readfirstlane(exact[step / sub]);
+    int blk = __builtin_amdgcn_readfirstlane(exact[step / sub]);
+    if ((unsigned)blk >= (unsigned)nKB) blk = nKB;
     return blk * Bk + (step % sub) * kKeysPerTile;
   }
 

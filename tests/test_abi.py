@@ -250,3 +250,67 @@ def test_decode_rejects():
     assert call(lam=2.0, splits=2) == sa.SA_ERR_UNSUPPORTED
     assert call(desc=_dec_desc(seqlen_q=4)) == sa.SA_ERR_UNSUPPORTED
     assert call(desc=_dec_desc(causal=1, seqlen_k=1)) == sa.SA_ERR_UNSUPPORTED
+
+
+# ---- the Python binding's own checks (run before any pointer is taken, so CPU tensors serve) ----
+
+def _bf(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def test_binding_rejects_mismatched_tensors():
+    q, k = _bf(1, 128, 2, 64), _bf(1, 256, 2, 64)
+    with pytest.raises(ValueError, match="v .* must have k's shape"):
+        sa.make_desc(q, k, _bf(1, 255, 2, 64), q)
+    with pytest.raises(ValueError, match="o .* must have q's shape"):
+        sa.make_desc(q, k, k, _bf(1, 128, 2, 128))
+    with pytest.raises(ValueError, match="batch/head_dim"):
+        sa.make_desc(q, _bf(2, 256, 2, 64))
+    with pytest.raises(ValueError, match="batch/head_dim"):
+        sa.make_desc(q, _bf(1, 256, 2, 128))
+
+
+def test_binding_checks_output_sizes():
+    import torch
+    q, k = _bf(1, 128, 2, 64), _bf(1, 256, 2, 64)
+    o = _bf(1, 128, 2, 64)
+    # nQT = 1 (block_q 128), nKT = 4
+    bad = [dict(tile_state=torch.zeros(1, 2, 1, 3, dtype=torch.uint8)),
+           dict(tile_state=torch.zeros(1, 2, 1, 4, dtype=torch.int32)),
+           dict(head_counters=torch.zeros(1, 2, 3, dtype=torch.int32)),
+           dict(lse=torch.zeros(1, 2, 127)),
+           dict(dbg_tile_rowmax=torch.zeros(1, 2, 1, 4, 64))]
+    for kw in bad:
+        with pytest.raises((ValueError, TypeError), match="must (hold|be)"):
+            sa.sa_skip_softmax_fwd(q, k, k, o, 0.5, **kw)
+    with pytest.raises(ValueError, match="must hold"):
+        sa.sa_nm_softmax_fwd(q, k, k, o, 2, 4, dbg_keep_bits=torch.zeros(1, 2, 128, 7,
+                                                                           dtype=torch.int32))
+    with pytest.raises(ValueError, match="must hold"):
+        sa.sa_nm_softmax_fwd(q, k, k, o, 2, 4, dbg_scores=torch.zeros(1, 2, 128, 255))
+    with pytest.raises(ValueError, match="must be contiguous"):
+        sa.sa_skip_softmax_fwd(q, k, k, o, 0.5, lse=torch.zeros(1, 128, 2).transpose(1, 2))
+    # correctly sized outputs pass the checks and only then meet the GPU-pointer check
+    with pytest.raises(ValueError, match="must live on the GPU"):
+        sa.sa_skip_softmax_fwd(q, k, k, o, 0.5,
+                               tile_state=torch.zeros(1, 2, 1, 4, dtype=torch.uint8),
+                               head_counters=torch.zeros(1, 2, 2, dtype=torch.int32),
+                               lse=torch.zeros(1, 2, 128), dbg_tile_rowmax=torch.zeros(2, 4, 128))
+
+
+def test_binding_checks_route_sizes():
+    import torch
+    kw = dict(batch=1, heads_kv=2, seqlen_q=300, seqlen_k=300, block_q=128, block_k=64)
+    # rows = 1*2*3 = 6, nKB = 5, W = 1
+    i32 = lambda *s: torch.zeros(s, dtype=torch.int32)   # noqa: E731
+    with pytest.raises(ValueError, match="exact_idx must hold"):
+        sa.sa_bitmask_route_prep(i32(6, 1), i32(6), i32(6, 4), i32(6, 1), **kw)
+    with pytest.raises(ValueError, match="bitmask must hold"):
+        sa.sa_bitmask_route_prep(i32(5, 1), i32(6), i32(6, 5), i32(6, 1), **kw)
+    with pytest.raises(ValueError, match="block_indptr must hold"):
+        sa.sa_bsr_route_prep(i32(6), i32(3), i32(6), i32(6, 5), i32(6, 1), **kw)
+    q, k = _bf(1, 300, 2, 64), _bf(1, 300, 2, 64)
+    with pytest.raises(ValueError, match="k_mean must hold"):
+        sa.sa_proxy_block_sparse_fwd(q, k, k, _bf(1, 2, 4, 64), _bf(1, 2, 5, 64), i32(6),
+                                     i32(6, 5), i32(6, 1), 1, q, block_q=128, block_k=64)

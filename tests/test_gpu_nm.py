@@ -103,13 +103,18 @@ def test_ties_lower_index_kept_m8(n):
     assert (g["bits"] == expect).all()
 
 
-def test_n_equals_m_matches_skip_kernel_at_lambda_zero():
-    announce("nm N=M vs dense")
+@pytest.mark.parametrize("n", [4, 8])
+def test_n_equals_m_is_dense_attention(n):
+    """N = M keeps every key: the GPU result equals the oracle's dense causal attention
+    (skip-softmax at lambda = 0, which never skips), and every keep bit of an allowed key is set."""
+    announce(f"nm N=M={n} vs dense oracle")
     q, k, v = W.gen_llm(35, 1, 384, 2, 2, 128)
-    g = run_gpu(q, k, v, True, 128, 8, 8, 0, 0, dbg=False)
-    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
-    o = torch.empty_like(qd)
-    sa.sa_skip_softmax_fwd(qd, kd, vd, o, 0.0, causal=True, block_q=128)
-    torch.cuda.synchronize()
-    mx, _ = err(g["o"], from_dev_bf16(o))
-    assert mx <= 1e-2
+    g = run_gpu(q, k, v, True, 128, n, n, 0, 0)
+    o_ref, lse_ref, _, _ = oracle.skip_softmax(q, k, v, causal=True, block_q=128, block_k=64,
+                                               scale=1 / math.sqrt(128), lam=0.0)
+    assert_output_parity(g["o"], o_ref, f"N=M={n}")
+    assert err(g["lse"], lse_ref)[0] < 2e-3
+    S = q.shape[1]
+    allowed = np.tril(np.ones((S, S), bool))
+    mask = np.unpackbits(g["bits"].view(np.uint8), axis=-1, bitorder="little")[..., :S].astype(bool)
+    assert (mask == allowed[None, None]).all()

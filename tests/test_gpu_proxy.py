@@ -167,19 +167,59 @@ def test_proxy_uneven_routes(D, use_proxy):
     assert lmx < 2e-3
 
 
-def test_all_ones_is_dense_and_empty_rows_are_zero():
-    announce("proxy all-ones / empty")
-    B, S, H, D, Bq, Bk = 1, 300, 2, 128, 128, 64
+@pytest.mark.parametrize("Bq,Bk", [(128, 64), (64, 64), (128, 128)])
+def test_all_ones_is_dense_and_empty_rows_are_zero(Bq, Bk):
+    """"Current integration stack": with every block exact, the proxy path is dense attention.  The
+    GPU result is compared with the oracle's proxy result and with the oracle's dense attention
+    (skip-softmax at lambda = 0, which never skips)."""
+    announce(f"proxy all-ones / empty Bq={Bq} Bk={Bk}")
+    B, S, H, D = 1, 300, 2, 128
     q, k, v = W.gen_iid(53, B, S, S, H, H, D)
     nQB, nKB = -(-S // Bq), -(-S // Bk)
     ones = np.full((B, H, nQB, 1), 0xFFFFFFFF, np.uint32)
-    o1, _, _, _ = run_proxy(q, k, v, ones, Bq, Bk, 1)
-    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
-    od = torch.empty_like(qd)
-    sa.sa_skip_softmax_fwd(qd, kd, vd, od, 0.0, causal=False, block_q=128)
-    torch.cuda.synchronize()
-    assert err(o1, from_dev_bf16(od))[0] <= 1e-2
+    o1, lse1, o_ref, lse_ref = run_proxy(q, k, v, ones, Bq, Bk, 1)
+    assert_output_parity(o1, o_ref, "proxy all-ones")
+    assert err(lse1, lse_ref)[0] < 2e-3
+    o_dense, lse_dense, _, _ = oracle.skip_softmax(q, k, v, causal=False, block_q=Bq, block_k=64,
+                                                   scale=1 / math.sqrt(D), lam=0.0)
+    assert_output_parity(o1, o_dense, "proxy all-ones vs dense oracle")
+    assert err(lse1, lse_dense)[0] < 2e-3
     empty = np.zeros((B, H, nQB, 1), np.uint32)
     empty[:, :, 1:] = 1
     o0, lse0, _, _ = run_proxy(q, k, v, empty, Bq, Bk, 0)
     assert (o0[:, :Bq] == 0).all() and np.isneginf(lse0[:, :, :Bq]).all()
+
+
+@pytest.mark.parametrize("use_proxy", [0, 1])
+@pytest.mark.parametrize("Bq,Bk", [(128, 128), (128, 64), (64, 64)])
+def test_inflated_n_exact_reads_nothing_past_the_route(Bq, Bk, use_proxy):
+    """A caller n_exact larger than the route's real count makes the kernel read the -1 fill after
+    the real exact_idx entries: such entries must contribute nothing (the result equals the one
+    with the true counts).  Only rows of batch 1 are inflated, so the K/V rows an unguarded kernel
+    would fetch in front of batch 1's slab still lie inside the allocation (batch 0)."""
+    announce(f"proxy inflated n_exact Bq={Bq} Bk={Bk} use_proxy={use_proxy}")
+    B, S, H, D = 2, 700, 2, 128
+    q, k, v = W.gen_iid(57, B, S, S, H, H, D)
+    nQB, nKB = -(-S // Bq), -(-S // Bk)
+    bm = W.gen_bitmask(57, B, H, nQB, nKB, max(1, nKB // 3))
+    km, vs = W.block_summaries(k, v, Bk)
+    ne, ix, kp = route_gpu(bm, B, H, S, S, Bq, Bk)
+    qd, kd, vd, kmd, vsd = to_dev(q), to_dev(k), to_dev(v), to_dev(km), to_dev(vs)
+    ne_bad = ne.clone()
+    ne_bad[1] = nKB + 5                       # past the real entries and past the row
+    ix_bad = ix.clone()
+    ix_bad[1, :, :, -1] = 1 << 20             # a far out-of-range entry inside the counted range
+    outs = []
+    for n_e, idx in ((ne, ix), (ne_bad, ix_bad)):
+        o = torch.full((B, S, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((B, H, S), float("nan"), device="cuda")
+        sa.sa_proxy_block_sparse_fwd(qd, kd, vd, kmd, vsd, n_e, idx, kp, use_proxy, o,
+                                     block_q=Bq, block_k=Bk, lse=lse)
+        torch.cuda.synchronize()
+        outs.append((from_dev_bf16(o), lse.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])
+    o_ref, lse_ref = oracle.proxy_fwd(q, k, v, km, vs, bm, block_q=Bq, block_k=Bk,
+                                      scale=1 / math.sqrt(D), use_proxy=use_proxy)
+    assert_output_parity(outs[1][0], o_ref, "inflated n_exact")
+    assert err(outs[1][1], lse_ref)[0] < 2e-3
