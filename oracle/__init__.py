@@ -12,6 +12,7 @@ Each wrapper returns results in natural layouts:
 * ``nm_softmax``: ``o``, ``lse``, ``keep_bits [B,Hq,Sq,ceil(Sk/32)]`` (uint32, LSB first).
 * ``skip_nm_softmax``: ``o``, ``lse``, ``tile_state``, ``rowmax`` as skip_softmax, plus
   ``keep_bits`` as nm_softmax.
+* ``skip_softmax_wave``: skip_softmax with every 32-row block deciding alone (block_q = 32).
 * ``skip_replay``: ``tile_state`` alone, replayed from given fp32 tile maxima (no dot products).
 * ``nm_keep_replay``: N:M keep bits alone, replayed from given fp32 scores (no dot products).
 * ``route_prep``: ``n_exact``, ``exact_idx`` (ascending, -1 padded), ``proxy_keep``.
@@ -204,6 +205,16 @@ def skip_nm_softmax(q, k, v, *, causal, block_q, block_k, scale, lam, n, m, sink
     kb = kb.reshape(B, Hq, nQT * block_q, W)[:, :, :Sq]
     return (np.ascontiguousarray(o), np.ascontiguousarray(lse), st.reshape(B, Hq, nQT, nKT),
             rm.reshape(B, Hq, nQT, nKT, block_q), np.ascontiguousarray(kb))
+
+
+def skip_softmax_wave(q, k, v, *, causal, block_k, scale, lam, mode=0, rowmax_in=None,
+                      state_in=None, units=None):
+    """Skip-softmax at wave granularity: every block of 32 query rows decides on its own, with its
+    own running max -- by definition the tile rule on 32-row query tiles (the reading of a
+    per-wave decision; the HuggingFace attention-sparsity page's "Custom Configuration" sets the
+    br x bc decision block).  Same outputs as skip_softmax with block_q = 32."""
+    return skip_softmax(q, k, v, causal=causal, block_q=32, block_k=block_k, scale=scale, lam=lam,
+                        mode=mode, rowmax_in=rowmax_in, state_in=state_in, units=units)
 
 
 def skip_replay(rowmax, *, batch, heads_q, seqlen_q, seqlen_k, causal, block_q, block_k, lam,

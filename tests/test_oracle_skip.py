@@ -105,10 +105,11 @@ def _closed_form_keep(q, k, causal, Br, Bc, lam, scale, dtype=np.float64):
     return keep, margin
 
 
+@pytest.mark.parametrize("Br,Bc", [(32, 32), (128, 128), (64, 128)])
 @pytest.mark.parametrize("lam", [0.25, 0.5, 0.8, 1.0])
 @pytest.mark.parametrize("causal", [True, False])
-def test_closed_form_decisions_for_lambda_at_most_one(lam, causal):
-    S, Br, Bc, D = 512, 32, 32, 128
+def test_closed_form_decisions_for_lambda_at_most_one(lam, causal, Br, Bc):
+    S, D = 512, 128
     q, k, v = W.gen_llm(21, 1, S, 2, 1, D)
     _, _, st, _ = _run(q, k, v, causal, Br, Bc, lam)
     keep, margin = _closed_form_keep(q, k, causal, Br, Bc, lam, 1 / math.sqrt(D))
@@ -328,3 +329,42 @@ def test_skip_replay_equals_full_oracle_replay(case, lam):
                               seqlen_k=Sk, causal=causal, block_q=Br, block_k=Bc, lam=lam,
                               units=units)
     assert np.array_equal(st_u, st_full.reshape(-1, nKT)[units])
+
+
+
+# ---- decision granularity: each 32-row block on its own (oracle.skip_softmax_wave) ---------------
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_wave_granularity_is_the_tile_rule_on_32_row_tiles(causal):
+    q, k, v = W.gen_llm(71, 1, 300, 2, 2, 64)
+    for lam in (0.0, 0.7, 2.0):
+        a = oracle.skip_softmax_wave(q, k, v, causal=causal, block_k=64, scale=0.125, lam=lam)
+        b = _run(q, k, v, causal, 32, 64, lam)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("Bc", [64, 128])
+def test_wave_granularity_lambda_zero_is_dense(Bc):
+    q, k, v = W.gen_llm(72, 1, 256, 2, 1, 64)
+    o, lse, st, _ = oracle.skip_softmax_wave(q, k, v, causal=True, block_k=Bc, scale=0.125,
+                                             lam=0.0)
+    assert (st != 1).all()
+    assert np.abs(o - refs.sdpa(q, k, v, 0.125, causal=True)).max() < 1e-12
+
+
+@pytest.mark.parametrize("lam", [0.3, 0.6, 0.9])
+@pytest.mark.parametrize("Bc", [64, 128])
+def test_wave_sparsity_at_least_tile_sparsity(lam, Bc):
+    """For lambda <= 1 every row's running max is the dense prefix max at either granularity, so a
+    tile that 128 rows skip together is skipped by each 32-row block that visits it: wave sparsity
+    (over the pairs a block visits) is at least tile sparsity.  Closed-form consequence, checked
+    on the oracle's decisions."""
+    q, k, v = W.gen_llm(73, 1, 1024, 2, 2, 128)
+    _, _, st_t, _ = _run(q, k, v, True, 128, Bc, lam)
+    _, _, st_w, _ = oracle.skip_softmax_wave(q, k, v, causal=True, block_k=Bc,
+                                             scale=1 / math.sqrt(128), lam=lam)
+    tile_skip = np.repeat(st_t == 1, 4, axis=2)
+    assert (st_w[tile_skip] != 0).all()
+    vis = st_w != 2
+    assert (st_w[vis] == 1).sum() >= tile_skip[vis].sum()
