@@ -53,6 +53,12 @@ typedef enum {
 /* Human-readable name of a status code (static string). */
 const char* sa_status_str(sa_status status);
 
+/* Decision granularity of skip-softmax (sa_skip_softmax_fwd_ex). */
+typedef enum {
+  SA_SKIP_GRAN_TILE = 0,  /* the whole block_q x block_k tile is kept or skipped */
+  SA_SKIP_GRAN_WAVE = 1   /* each block of 32 query rows (one wavefront) decides on its own */
+} sa_skip_granularity;
+
 /* Shape and layout of one attention call. */
 typedef struct {
   int32_t batch, heads_q, heads_kv;
@@ -60,7 +66,7 @@ typedef struct {
   int32_t head_dim;        /* 64 or 128 */
   int32_t causal;          /* 0 or 1 */
   int32_t block_q;         /* query tile (skip, N:M) or query block (proxy) rows: 64 or 128 */
-  int32_t block_k;         /* key tile (skip, N:M: 64) or semantic KV block (proxy: 64 or 128) */
+  int32_t block_k;         /* key tile (skip, N:M) or semantic KV block (proxy): 64 or 128 */
   float softmax_scale;     /* > 0 and finite, usually 1/sqrt(head_dim) */
   int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];  /* batch, seq, head (elements) */
 } sa_attn_desc;
@@ -85,12 +91,35 @@ typedef struct {
  *                     over the kept keys.
  *   dbg_tile_rowmax   optional debug export, fp32 [B, Hq, nQT, nKT, block_q]: the M_j[r] the
  *                     decision used (log2 domain); -inf for unvisited tiles and empty rows.
- * Supported: head_dim 64/128, block_q 64/128, block_k 64.
+ * Supported: head_dim 64/128, block_q 64/128, block_k 64/128 (the Model-Optimizer HuggingFace
+ * attention-sparsity page, "Custom Configuration", uses br = bc = 128).
  */
 sa_status sa_skip_softmax_fwd(const sa_attn_desc* desc, const void* q, const void* k,
                               const void* v, void* o, float lambda, uint8_t* tile_state,
                               uint32_t* head_counters, float* lse, float* dbg_tile_rowmax,
                               void* stream);
+
+/*
+ * Skip-softmax forward with a choice of decision granularity (the same rule; the HuggingFace
+ * attention-sparsity page, "Custom Configuration", sets the br x bc block the decisions are made
+ * on).  granularity SA_SKIP_GRAN_TILE is sa_skip_softmax_fwd.  SA_SKIP_GRAN_WAVE decides every
+ * block of R = 32 query rows on its own -- its own running max, its own skips -- exactly as
+ * sa_skip_softmax_fwd with 32-row query tiles would; block_q then only sets how many such blocks
+ * share one pass over K/V, and a V tile is loaded when any of them keeps it.
+ *
+ *   granularity       SA_SKIP_GRAN_TILE or SA_SKIP_GRAN_WAVE (SA_ERR_VALUE otherwise).
+ *   tile_state        optional, uint8 [B, Hq, nR, nKT] with nR = ceil(Sq/R), R = block_q (tile) or
+ *                     32 (wave): 0 kept, 1 skipped, 2 not visited (no unmasked key of the block).
+ *   head_counters     optional, uint32 [B, Hq, 2]: {visited, skipped} (R-row block, key tile)
+ *                     pairs, added to.
+ *   lse               optional, fp32 [B, Hq, Sq].
+ *   dbg_tile_rowmax   optional, fp32 [B, Hq, nR, nKT, R].
+ * Other arguments and the supported sizes as sa_skip_softmax_fwd.
+ */
+sa_status sa_skip_softmax_fwd_ex(const sa_attn_desc* desc, const void* q, const void* k,
+                                 const void* v, void* o, float lambda, int32_t granularity,
+                                 uint8_t* tile_state, uint32_t* head_counters, float* lse,
+                                 float* dbg_tile_rowmax, void* stream);
 
 /*
  * N:M sparse softmax forward (Model-Optimizer HuggingFace attention sparsity: "N:M Sparse
@@ -106,7 +135,8 @@ sa_status sa_skip_softmax_fwd(const sa_attn_desc* desc, const void* q, const voi
  *                     k>>5 set when key k is kept (LSB first); padding bits 0.
  *   dbg_scores        optional debug export, fp32 [B, Hq, Sq, Sk]: the raw q.k the ranking used
  *                     (-inf where causally masked).
- * Supported: head_dim 64/128, block_q 64/128, block_k 64.
+ * Supported: head_dim 64/128, block_q 64/128, block_k 64/128 (the result does not depend on
+ * block_k, which the rule does not use).
  */
 sa_status sa_nm_softmax_fwd(const sa_attn_desc* desc, const void* q, const void* k,
                             const void* v, void* o, int32_t n, int32_t m,
@@ -126,7 +156,7 @@ sa_status sa_nm_softmax_fwd(const sa_attn_desc* desc, const void* q, const void*
  *   (n, m), dense_sink_tokens, dense_recent_tokens, dbg_keep_bits, dbg_scores
  *                     as sa_nm_softmax_fwd; dbg_keep_bits are the N:M bits of every visited
  *                     tile, whether the tile was then kept or skipped.
- * Supported: head_dim 64/128, block_q 64/128, block_k 64.
+ * Supported: head_dim 64/128, block_q 64/128, block_k 64/128 (decision tiles as sa_skip_softmax_fwd).
  */
 sa_status sa_skip_nm_softmax_fwd(const sa_attn_desc* desc, const void* q, const void* k,
                                  const void* v, void* o, float lambda, int32_t n, int32_t m,

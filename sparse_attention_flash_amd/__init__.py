@@ -25,6 +25,10 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
+SA_SKIP_GRAN_TILE, SA_SKIP_GRAN_WAVE = 0, 1
+GRANULARITY = {"tile": SA_SKIP_GRAN_TILE, "wave": SA_SKIP_GRAN_WAVE}
+WAVE_ROWS = 32   # decision rows at wave granularity
+
 SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_ALIGN, SA_ERR_VALUE, SA_ERR_HIP = range(7)
 STATUS_NAMES = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_UNSUPPORTED",
                 4: "SA_ERR_ALIGN", 5: "SA_ERR_VALUE", 6: "SA_ERR_HIP"}
@@ -50,6 +54,8 @@ _lib.sa_status_str.argtypes = [ctypes.c_int]
 _lib.sa_status_str.restype = ctypes.c_char_p
 _lib.sa_skip_softmax_fwd.argtypes = [_DESC, _P, _P, _P, _P, _F, _P, _P, _P, _P, _P]
 _lib.sa_skip_softmax_fwd.restype = ctypes.c_int
+_lib.sa_skip_softmax_fwd_ex.argtypes = [_DESC, _P, _P, _P, _P, _F, _I32, _P, _P, _P, _P, _P]
+_lib.sa_skip_softmax_fwd_ex.restype = ctypes.c_int
 _lib.sa_nm_softmax_fwd.argtypes = [_DESC, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P]
 _lib.sa_nm_softmax_fwd.restype = ctypes.c_int
 _lib.sa_skip_nm_softmax_fwd.argtypes = [_DESC, _P, _P, _P, _P, _F, _I32, _I32, _I32, _I32, _P, _P,
@@ -194,6 +200,21 @@ def sa_skip_softmax_fwd(q, k, v, o, lam, *, causal=False, block_q=128, block_k=6
                                     float(lam), _ptr(tile_state), _ptr(head_counters), _ptr(lse),
                                     _ptr(dbg_tile_rowmax), _stream(stream)),
            "sa_skip_softmax_fwd")
+
+
+def sa_skip_softmax_fwd_ex(q, k, v, o, lam, granularity="tile", *, causal=False, block_q=128,
+                           block_k=64, scale=None, tile_state=None, head_counters=None, lse=None,
+                           dbg_tile_rowmax=None, stream=None):
+    """Skip-softmax with decisions per query tile ("tile") or per 32-row wavefront ("wave");
+    tile_state / dbg_tile_rowmax are per decision block of rows (sa.h)."""
+    gran = GRANULARITY[granularity] if isinstance(granularity, str) else int(granularity)
+    d = make_desc(q, k, v, o, causal=causal, block_q=block_q, block_k=block_k, scale=scale)
+    rows = WAVE_ROWS if gran == SA_SKIP_GRAN_WAVE else d.block_q
+    _skip_outputs(d, rows, tile_state, head_counters, lse, dbg_tile_rowmax)
+    _check(_lib.sa_skip_softmax_fwd_ex(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                       float(lam), gran, _ptr(tile_state), _ptr(head_counters),
+                                       _ptr(lse), _ptr(dbg_tile_rowmax), _stream(stream)),
+           "sa_skip_softmax_fwd_ex")
 
 
 def sa_nm_softmax_fwd(q, k, v, o, n, m, dense_sink_tokens=0, dense_recent_tokens=0, *,

@@ -160,22 +160,32 @@ const char* sa_status_str(sa_status status) {
   return "unknown sa_status";
 }
 
-sa_status sa_skip_softmax_fwd(const sa_attn_desc* desc, const void* q, const void* k,
-                              const void* v, void* o, float lambda, uint8_t* tile_state,
-                              uint32_t* head_counters, float* lse, float* dbg_tile_rowmax,
-                              void* stream) {
+sa_status sa_skip_softmax_fwd_ex(const sa_attn_desc* desc, const void* q, const void* k,
+                                 const void* v, void* o, float lambda, int32_t granularity,
+                                 uint8_t* tile_state, uint32_t* head_counters, float* lse,
+                                 float* dbg_tile_rowmax, void* stream) {
   sa_status st = check_attention(desc, q, k, v, o);
   if (st != SA_OK) return st;
-  if (desc->block_k != 64) return SA_ERR_UNSUPPORTED;
+  if (desc->block_k != 64 && desc->block_k != 128) return SA_ERR_UNSUPPORTED;
+  if (granularity != SA_SKIP_GRAN_TILE && granularity != SA_SKIP_GRAN_WAVE) return SA_ERR_VALUE;
   if (!(lambda >= 0.f) || !std::isfinite(lambda)) return SA_ERR_VALUE;
   sa::SkipArgs a{};
   a.g = geometry(desc, q, k, v, o);
   a.L32 = lambda == 0.f ? -INFINITY : (float)std::log2((double)lambda);
+  a.wave_gran = granularity == SA_SKIP_GRAN_WAVE;
   a.tile_state = tile_state;
   a.counters = head_counters;
   a.lse = lse;
   a.rowmax = dbg_tile_rowmax;
   return from_hip(sa::launch_skip_softmax(a, (hipStream_t)stream));
+}
+
+sa_status sa_skip_softmax_fwd(const sa_attn_desc* desc, const void* q, const void* k,
+                              const void* v, void* o, float lambda, uint8_t* tile_state,
+                              uint32_t* head_counters, float* lse, float* dbg_tile_rowmax,
+                              void* stream) {
+  return sa_skip_softmax_fwd_ex(desc, q, k, v, o, lambda, SA_SKIP_GRAN_TILE, tile_state,
+                                head_counters, lse, dbg_tile_rowmax, stream);
 }
 
 sa_status sa_nm_softmax_fwd(const sa_attn_desc* desc, const void* q, const void* k,
@@ -184,7 +194,7 @@ sa_status sa_nm_softmax_fwd(const sa_attn_desc* desc, const void* q, const void*
                             uint32_t* dbg_keep_bits, float* dbg_scores, void* stream) {
   sa_status st = check_attention(desc, q, k, v, o);
   if (st != SA_OK) return st;
-  if (desc->block_k != 64) return SA_ERR_UNSUPPORTED;
+  if (desc->block_k != 64 && desc->block_k != 128) return SA_ERR_UNSUPPORTED;
   if (!((m == 4 && n >= 1 && n <= 4) || (m == 8 && n >= 1 && n <= 8))) return SA_ERR_UNSUPPORTED;
   if (dense_sink_tokens < 0 || dense_recent_tokens < 0) return SA_ERR_VALUE;
   sa::NmArgs a{};
@@ -207,7 +217,7 @@ sa_status sa_skip_nm_softmax_fwd(const sa_attn_desc* desc, const void* q, const 
                                  float* dbg_scores, void* stream) {
   sa_status st = check_attention(desc, q, k, v, o);
   if (st != SA_OK) return st;
-  if (desc->block_k != 64) return SA_ERR_UNSUPPORTED;
+  if (desc->block_k != 64 && desc->block_k != 128) return SA_ERR_UNSUPPORTED;
   if (!((m == 4 && n >= 1 && n <= 4) || (m == 8 && n >= 1 && n <= 8))) return SA_ERR_UNSUPPORTED;
   if (dense_sink_tokens < 0 || dense_recent_tokens < 0) return SA_ERR_VALUE;
   if (!(lambda >= 0.f) || !std::isfinite(lambda)) return SA_ERR_VALUE;
@@ -382,7 +392,7 @@ sa_status sa_skip_softmax_calibrate(const sa_attn_desc* desc, const void* q, con
     if (!(trial_lambdas[i] >= 0.f) || !std::isfinite(trial_lambdas[i])) return SA_ERR_VALUE;
   sa_status st = check_attention(desc, q, k, v, o);
   if (st != SA_OK) return st;
-  if (desc->block_k != 64) return SA_ERR_UNSUPPORTED;
+  if (desc->block_k != 64 && desc->block_k != 128) return SA_ERR_UNSUPPORTED;
   const hipStream_t s = (hipStream_t)stream;
   const size_t n_heads = (size_t)desc->batch * desc->heads_q;
   std::vector<uint32_t> host(2 * n_heads);

@@ -21,6 +21,7 @@ struct AttnGeom {
 struct SkipArgs {
   AttnGeom g;
   float L32;                            // log2(lambda) in fp32; -inf when lambda == 0
+  int wave_gran;                        // 1: each 32-row wavefront decides alone
   uint8_t* tile_state;
   uint32_t* counters;
   float* lse;

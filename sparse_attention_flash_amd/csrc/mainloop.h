@@ -123,11 +123,13 @@ __device__ __forceinline__ void tile_row_max(const f32x16 (&s)[2][QB], float c32
   }
 }
 
-// Per-tile state: row maxima (log2 domain) and the decision.
+// Per-step state: row maxima (log2 domain) and the decision.
 template <int QB>
 struct TileState {
   float M[QB];
-  bool keep;
+  bool keep;      // this wave runs the step's softmax and P.V
+  bool fetched;   // the step's V tile was requested
+  bool own;       // this wave's published vote
 };
 
 // Softmax of a kept tile fused with its P.V product.  For each 16-key chunk: exponentials of the
@@ -229,12 +231,26 @@ __device__ __forceinline__ void softmax_pv(const Pol& pol, int step, const f32x1
 //   int steps() const;  TileSrc src(int step) const;
 //   void mask(int step, f32x16 (&s)[2][QB], int lane) const;        -inf for masked keys
 //   static constexpr bool kDecide, kFilter, kWeighted;
+//   static constexpr bool kWave, kPair;                                            [kDecide]
 //   bool negligible(const float (&M)[QB], const float (&mt)[QB], int lane) const;   [kDecide]
+//   bool visible(int step) const;   the step holds an unmasked key of this wave's rows [kDecide]
 //   void filter(int step, f32x16 (&s)[2][QB], int lane) const;  dropped keys -> -inf   [kFilter]
 //   bool weighted(int step) const; float weight(int step, int kb, int r, int lane) const; [kWeighted]
-//   void record(int step, bool keep, const float (&M)[QB], int wave, int lane, bool leader);
+//   void record(int tile, bool keep, const float (&M)[QB], int wave, int lane, bool leader);
 // On return o, mref and l hold the unnormalised accumulator, exponent reference and row-sum
 // partials of this lane (l still to be summed over the two lane halves).
+//
+// Decisions (kDecide).  Every wave publishes one vote per step in LDS; after the next barrier:
+//   - tile granularity (!kWave): the step is kept for every wave when any wave voted "some row
+//     not negligible";
+//   - wave granularity (kWave): each wave keeps the step on its own vote (its 32 rows alone) and
+//     the V tile is fetched when any wave keeps it.
+// A kept step raises the wave's decision max mt at once.  With kPair the decision tile is 128 keys,
+// two consecutive 64-key steps (2p, 2p+1) decided together against the running max from before
+// the pair: the pair is skipped only when both halves are negligible (max over the 128 keys below
+// the threshold is the same as both halves below it).  Half a is decided first; when it is kept
+// the pair is kept.  Otherwise half b's vote decides, and a pair kept only through half b ("late"
+// keep) requests V of half a then, waiting for it before that half's softmax.
 template <int D, int NW, int QB, class Pol>
 struct Mainloop {
   using DmaK = Dma<KLayout<D>, NW>;
@@ -253,7 +269,9 @@ struct Mainloop {
   float (&l)[QB];
   float c32;
   int wave, lane, tid, n;
-  float mt[QB];   // running max of kept tiles' maxima (decision state)
+  float mt[QB];         // running max of kept tiles' maxima (decision state)
+  bool pair_own = false;       // kPair: this wave keeps the pair being decided (from half a)
+  bool pair_fetched = false;   // kPair: V of half a was requested
 
   __device__ __forceinline__ void issue_k(int step) {
     const TileSrc t = pol.src(step);
@@ -273,31 +291,70 @@ struct Mainloop {
     if constexpr (Pol::kFilter) pol.filter(step, s, lane);
   }
 
-  // Each wave publishes "some row of this tile is not negligible" in LDS; the votes are read
-  // after the next barrier.
-  __device__ __forceinline__ void vote(int step, const TS& ts) {
+  // Each wave publishes "some row of this tile is not negligible" in LDS (for the second half of a
+  // pair: "this wave keeps the pair"); the votes are read after the next barrier.
+  __device__ __forceinline__ void vote(int step, TS& ts) {
     if constexpr (Pol::kDecide) {
-      const bool wave_keep = __builtin_amdgcn_ballot_w64(!pol.negligible(ts.M, mt, lane)) != 0ull;
-      if (lane == 0) sm.vote[step & 1][wave] = wave_keep ? 1 : 0;
+      bool own = __builtin_amdgcn_ballot_w64(!pol.negligible(ts.M, mt, lane)) != 0ull;
+      if constexpr (Pol::kWave) own = own && pol.visible(step);
+      if constexpr (Pol::kPair) {
+        if (step & 1) own = own || pair_own;
+      }
+      ts.own = own;
+      if (lane == 0) sm.vote[step & 1][wave] = own ? 1 : 0;
     }
   }
 
-  // After a barrier that follows every wave's vote(step): the decision.  A kept tile raises the
-  // decision max mt at once and has its V tile fetched.
-  __device__ __forceinline__ void resolve(int step, TS& ts) {
-    ts.keep = true;
-    if constexpr (Pol::kDecide) {
-      int any = 0;
+  __device__ __forceinline__ void raise_mt(const float (&M)[QB]) {
 #pragma unroll
-      for (int w = 0; w < NW; ++w) any |= sm.vote[step & 1][w];
-      ts.keep = any != 0;
-    }
-    if (ts.keep) {
+    for (int qb = 0; qb < QB; ++qb) mt[qb] = fmaxf(mt[qb], M[qb]);
+  }
+
+  // After a barrier that follows every wave's vote(step): the decision.  A kept step raises the
+  // decision max mt at once and has its V tile fetched.  `other` is the state of the pair's other
+  // half (kPair).  Returns true for a late keep: V of half a was requested only now.
+  __device__ __forceinline__ bool resolve(int step, TS& ts, TS& other) {
+    int any = 0;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) mt[qb] = fmaxf(mt[qb], ts.M[qb]);
-      issue_v(step);
+    for (int w = 0; w < NW; ++w) any |= sm.vote[step & 1][w];
+    const bool fetch = any != 0;
+    const bool mine = Pol::kWave ? ts.own : fetch;
+    ts.keep = mine;
+    ts.fetched = fetch;
+    if constexpr (!Pol::kPair) {
+      if (mine) raise_mt(ts.M);
+      if (fetch) issue_v(step);
+      pol.record(step, mine, ts.M, wave, lane, tid == 0);
+      return false;
+    } else {
+      if (!(step & 1)) {   // half a
+        pair_own = mine;
+        pair_fetched = fetch;
+        if (mine) raise_mt(ts.M);
+        if (fetch) issue_v(step);
+        if (step + 1 >= n) pol.record(step >> 1, mine, ts.M, wave, lane, tid == 0);
+        return false;
+      }
+      // half b: `mine` already includes half a's keep (the published vote ORs it in)
+      if (mine) {
+        if (!pair_own) {   // kept through half b only: half a is kept too
+          raise_mt(other.M);
+          other.keep = true;
+        }
+        raise_mt(ts.M);
+      }
+      const bool late = fetch && !pair_fetched;
+      if (late) {
+        issue_v(step - 1);
+        other.fetched = true;
+      }
+      if (fetch) issue_v(step);
+      float Mp[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) Mp[qb] = fmaxf(other.M[qb], ts.M[qb]);
+      pol.record(step >> 1, mine, Mp, wave, lane, tid == 0);
+      return late;
     }
-    pol.record(step, ts.keep, ts.M, wave, lane, tid == 0);
   }
 
   // iteration j.  On entry S(j) is in sa with keep(j) resolved (V(j) requested when kept), S(j+1)
@@ -307,9 +364,18 @@ struct Mainloop {
     wait_vmcnt<0>();
     lds_barrier();
     // 2: decide j+1 and request its V tile (the buffer V(j-1) used)
-    if (j + 1 < n) resolve(j + 1, tb);
+    bool late = false;
+    if (j + 1 < n) late = resolve(j + 1, tb, ta);
     // 3: request K(j+3) (the buffer K(j+1) used)
     if (j + 3 < n) issue_k(j + 3);
+    if constexpr (Pol::kPair) {
+      // a late keep requested V(j) just now (into the buffer V(j-2) used, free since the barrier of
+      // iteration j-1), ahead of V(j+1) and K(j+3): wait for it alone
+      if (late) {
+        if (j + 3 < n) wait_vmcnt<2 * kN>(); else wait_vmcnt<kN>();
+        lds_barrier();
+      }
+    }
     // 4: softmax(j) fused with O += P(j) V(j)
     if (ta.keep) softmax_pv<D, QB>(pol, j, sa, ta, mref, l, o, sm.v[j & 1], c32, lane);
     // 5: S(j+2) into sa, its row maxima and votes (mt already holds every kept tile up to j+1)
@@ -347,20 +413,20 @@ struct Mainloop {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mt[qb] = -INFINITY;
     if (n <= 0) return;
-    if constexpr (!Pol::kDecide) {
-      {
-        const TileSrc t = pol.src(0);
-        klo = DmaK::lane_offsets(t.k_stride_b, wave, lane);
-        vlo = DmaV::lane_offsets(t.v_stride_b, wave, lane);
-      }
-      run_dense();
-      return;
-    }
     {
       const TileSrc t = pol.src(0);
       klo = DmaK::lane_offsets(t.k_stride_b, wave, lane);
       vlo = DmaV::lane_offsets(t.v_stride_b, wave, lane);
     }
+    if constexpr (!Pol::kDecide) {
+      run_dense();
+    } else {
+      run_decide();
+    }
+  }
+
+  // The decision pipeline: scores two steps ahead of the softmax.
+  __device__ __forceinline__ void run_decide() {
     f32x16 sa[2][QB], sb[2][QB];
     TS ta, tb;
     // prologue: K(0), K(1); S(0) and keep(0) (V(0) requested); S(1) and its votes; K(2)
@@ -371,10 +437,10 @@ struct Mainloop {
     scores(0, sa, ta);
     vote(0, ta);
     lds_barrier();
-    resolve(0, ta);
+    resolve(0, ta, tb);
     if (n > 1) {
-      // K(1) landed: only V(0) (if kept) was requested after it
-      if (ta.keep) wait_vmcnt<kN>(); else wait_vmcnt<0>();
+      // K(1) landed: only V(0) (if requested) was requested after it
+      if (ta.fetched) wait_vmcnt<kN>(); else wait_vmcnt<0>();
       lds_barrier();
       scores(1, sb, tb);
       vote(1, tb);

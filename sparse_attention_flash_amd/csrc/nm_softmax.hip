@@ -8,7 +8,8 @@
 // keys rank last), ties to the lower key index, "recent" = 0 <= row - key < R.
 //
 // Same pipelined loop as the skip-softmax kernel (mainloop.h), every visited tile kept; the rule
-// is NmFilter (policies.h).
+// is NmFilter (policies.h).  Nothing here depends on the key tile: block_k 64 and 128 run the same
+// kernel and give the same result.
 #include "policies.h"
 
 namespace sa {

@@ -130,28 +130,53 @@ struct KeyTiles {
 };
 
 // ---- the skip rule --------------------------------------------------------------------------------
+//
+// Decision tiles are block_k = 64 keys (one step) or 128 keys (kPair: two steps decided together).
+// Decision rows are the whole query tile (tile granularity) or each wavefront's 32 rows alone
+// (kWave, wave granularity: a 32-row block is decided exactly as a query tile of 32 rows would
+// be, and the V tile is fetched for the workgroup when any wave keeps it).  The state, counter and
+// maxima exports are per decision block of rows: tile_state [B, Hq, nR, nKTd] with nR =
+// ceil(Sq/R), R = block_q or 32, nKTd = ceil(Sk/block_k); rowmax [.., nKTd, R].
 
-template <int D, int NW, int QB>
+template <int D, int NW, int QB, bool kWaveGran = false, bool kPairTiles = false>
 struct SkipDecision : KeyTiles<QB> {
   static constexpr bool kDecide = true, kFilter = false, kWeighted = false;
+  static constexpr bool kWave = kWaveGran, kPair = kPairTiles;
+  static_assert(!kWave || QB == 1, "wave granularity decides 32-row blocks");
   static constexpr int RW = 32 * QB;
   static constexpr int BR = NW * RW;
+  static constexpr int R = kWave ? RW : BR;        // decision rows
+  static constexpr int kSub = kPair ? 2 : 1;       // steps per decision tile
   float L32;
   uint8_t* tile_state;
   float* rowmax;
-  int64_t unit;
-  int nKT, nskip;
+  int64_t unit;      // decision row block: (b*Hq + hq)*nR + (qt*NW + wave when kWave, else qt)
+  int nKTd;          // decision tiles per row block
+  int nvis_w;        // steps with an unmasked key of this wave's rows (kWave), else of the tile
+  bool exists;       // this decision block has a row < Sq
+  int nskip;
 
   // Args: SkipArgs or SkipNmArgs
   template <class Args>
   __device__ __forceinline__ void init(const Args& a, const TileUnit& u, int lane) {
     this->init_tiles(a.g, u, D, lane);
-    nKT = u.nKT;
+    nKTd = (a.g.Sk + kSub * kKeysPerTile - 1) / (kSub * kKeysPerTile);
     L32 = a.L32;
     tile_state = a.tile_state;
     rowmax = a.rowmax;
-    unit = u.unit;
     nskip = 0;
+    if constexpr (kWave) {
+      const int wave = (u.wrow0 - u.row0) / RW;
+      const int n32 = (a.g.Sq + RW - 1) / RW;
+      unit = ((int64_t)u.b * a.g.Hq + u.hq) * n32 + (int64_t)u.qt * NW + wave;
+      exists = u.wrow0 < a.g.Sq;
+      const int last = min(u.wrow0 + RW, a.g.Sq) - 1;
+      nvis_w = !exists ? 0 : (a.g.causal ? min(u.nKT, last / kKeysPerTile + 1) : u.nKT);
+    } else {
+      unit = u.unit;
+      exists = true;
+      nvis_w = u.nvis;
+    }
   }
 
   // true when every valid row this lane holds is negligible: M < fl32(m + log2(lambda))
@@ -166,28 +191,44 @@ struct SkipDecision : KeyTiles<QB> {
     return negl;
   }
 
-  __device__ __forceinline__ void record(int j, bool keep, const float (&M)[QB], int wave, int,
-                                         bool leader) {
+  // the step holds an unmasked key of this wave's rows (wave granularity)
+  __device__ __forceinline__ bool visible(int step) const { return step < nvis_w; }
+
+  // decision tiles this block of rows visits
+  __device__ __forceinline__ int nvis_d() const { return (nvis_w + kSub - 1) / kSub; }
+
+  // the final decision of decision tile j (M: its row maxima over all of its keys)
+  __device__ __forceinline__ void record(int j, bool keep, const float (&M)[QB], int wave,
+                                         int lane, bool leader) {
+    if constexpr (kWave) {
+      if (!exists || j >= nvis_d()) return;   // not part of this block's visited tiles
+      leader = lane == 0;
+    }
     if (!keep) ++nskip;
-    if (leader && tile_state != nullptr) tile_state[unit * nKT + j] = keep ? 0 : 1;
+    if (leader && tile_state != nullptr) tile_state[unit * nKTd + j] = keep ? 0 : 1;
     if (rowmax != nullptr && this->h == 0) {
+      const int r0 = kWave ? 0 : wave * RW;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-        rowmax[(unit * nKT + j) * BR + wave * RW + qb * 32 + this->r32] = M[qb];
+        rowmax[(unit * nKTd + j) * R + r0 + qb * 32 + this->r32] = M[qb];
     }
   }
 
   // tiles never visited (causal): state 2, maxima -inf; the head counters
   template <class Args>
   __device__ __forceinline__ void finish(const Args& a, const TileUnit& u, int tid) const {
-    constexpr int NT = NW * 64;
+    if (!exists) return;
+    // tile granularity: the workgroup's threads share the row block; wave granularity: the wave's
+    constexpr int NT = kWave ? 64 : NW * 64;
+    const int t = kWave ? (tid & 63) : tid;
+    const int nv = nvis_d();
     if (a.tile_state != nullptr)
-      for (int j = u.nvis + tid; j < nKT; j += NT) a.tile_state[unit * nKT + j] = 2;
+      for (int j = nv + t; j < nKTd; j += NT) a.tile_state[unit * nKTd + j] = 2;
     if (a.rowmax != nullptr)
-      for (int64_t i = (int64_t)u.nvis * BR + tid; i < (int64_t)nKT * BR; i += NT)
-        a.rowmax[unit * nKT * BR + i] = -INFINITY;
-    if (tid == 0 && a.counters != nullptr) {
-      atomicAdd(&a.counters[2 * (u.b * a.g.Hq + u.hq)], (unsigned)u.nvis);
+      for (int64_t i = (int64_t)nv * R + t; i < (int64_t)nKTd * R; i += NT)
+        a.rowmax[unit * nKTd * R + i] = -INFINITY;
+    if (t == 0 && a.counters != nullptr) {
+      atomicAdd(&a.counters[2 * (u.b * a.g.Hq + u.hq)], (unsigned)nv);
       atomicAdd(&a.counters[2 * (u.b * a.g.Hq + u.hq) + 1], (unsigned)nskip);
     }
   }
@@ -532,8 +573,8 @@ struct NmFilter {
 
 // ---- the policies -----------------------------------------------------------------------------------
 
-template <int D, int NW, int QB>
-using SkipPolicy = SkipDecision<D, NW, QB>;
+template <int D, int NW, int QB, bool kWave = false, bool kPair = false>
+using SkipPolicy = SkipDecision<D, NW, QB, kWave, kPair>;
 
 template <int D, int NW, int QB, int M>
 struct NmPolicy : KeyTiles<QB> {
@@ -554,20 +595,21 @@ struct NmPolicy : KeyTiles<QB> {
 
 // Both rules: the skip decision on the tile maxima (equal to the maxima over the N:M-kept keys),
 // the N:M bits inside every kept tile.
-template <int D, int NW, int QB, int M>
-struct SkipNmPolicy : SkipDecision<D, NW, QB> {
+template <int D, int NW, int QB, int M, bool kPair = false>
+struct SkipNmPolicy : SkipDecision<D, NW, QB, false, kPair> {
+  using Skip = SkipDecision<D, NW, QB, false, kPair>;
   static constexpr bool kDecide = true, kFilter = true, kWeighted = false;
   NmFilter<NW, QB, M> nm;
 
   __device__ __forceinline__ void init(const SkipNmArgs& a, const TileUnit& u, int lane) {
-    SkipDecision<D, NW, QB>::init(a, u, lane);
+    Skip::init(a, u, lane);
     nm.init(a, u);
   }
   __device__ __forceinline__ void filter(int j, f32x16 (&s)[2][QB], int lane) const {
     nm.filter(*this, j, s, lane);
   }
   __device__ __forceinline__ void finish(const SkipNmArgs& a, const TileUnit& u, int tid) const {
-    SkipDecision<D, NW, QB>::finish(a, u, tid);
+    Skip::finish(a, u, tid);
     nm.finish(a, u, tid);
   }
 };

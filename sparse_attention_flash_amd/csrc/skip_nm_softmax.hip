@@ -12,26 +12,29 @@
 namespace sa {
 namespace {
 
-template <int D, int NW, int QB, int M>
+template <int D, int NW, int QB, int M, bool kPair>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<QB>)))
 void skip_nm_softmax_kernel(SkipNmArgs a) {
   __shared__ __attribute__((aligned(1024))) Smem<D, NW> sm;
-  attention_tile<D, NW, QB, SkipNmPolicy<D, NW, QB, M>>(a, sm);
+  attention_tile<D, NW, QB, SkipNmPolicy<D, NW, QB, M, kPair>>(a, sm);
 }
 
-template <int D, int NW, int QB, int M>
+template <int D, int NW, int QB, int M, bool kPair>
 hipError_t launch_t(const SkipNmArgs& a, hipStream_t stream) {
   constexpr int BR = NW * 32 * QB;
   const int nQT = (a.g.Sq + BR - 1) / BR;
   const int total = a.g.B * a.g.Hq * nQT;
-  hipLaunchKernelGGL((skip_nm_softmax_kernel<D, NW, QB, M>), dim3(total), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((skip_nm_softmax_kernel<D, NW, QB, M, kPair>), dim3(total), dim3(NW * 64), 0,
                      stream, a);
   return hipGetLastError();
 }
 
 template <int D, int NW, int QB>
 hipError_t launch_m(const SkipNmArgs& a, hipStream_t stream) {
-  return a.m == 8 ? launch_t<D, NW, QB, 8>(a, stream) : launch_t<D, NW, QB, 4>(a, stream);
+  const bool pair = a.g.block_k == 128;   // 128-key decision tiles: two 64-key steps together
+  if (a.m == 8)
+    return pair ? launch_t<D, NW, QB, 8, true>(a, stream) : launch_t<D, NW, QB, 8, false>(a, stream);
+  return pair ? launch_t<D, NW, QB, 4, true>(a, stream) : launch_t<D, NW, QB, 4, false>(a, stream);
 }
 
 }  // namespace

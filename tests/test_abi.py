@@ -68,7 +68,8 @@ def _skip(d, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lam=0.1):
     (dict(causal=2), sa.SA_ERR_VALUE),
     (dict(head_dim=96), sa.SA_ERR_UNSUPPORTED),
     (dict(block_q=32), sa.SA_ERR_UNSUPPORTED),
-    (dict(block_k=128), sa.SA_ERR_UNSUPPORTED),
+    (dict(block_k=32), sa.SA_ERR_UNSUPPORTED),
+    (dict(block_k=256), sa.SA_ERR_UNSUPPORTED),
     (dict(softmax_scale=0.0), sa.SA_ERR_VALUE),
     (dict(softmax_scale=float("nan")), sa.SA_ERR_VALUE),
     (dict(q_stride=(256 * 4 * 128, 4 * 128, 4)), sa.SA_ERR_ALIGN),
@@ -184,7 +185,7 @@ def test_calibrate_rejects():
     assert call([0.1, -1.0]) == sa.SA_ERR_VALUE
     assert call([float("nan")]) == sa.SA_ERR_VALUE
     assert call([0.1], desc=None) == sa.SA_ERR_NULL
-    assert call([0.1], desc=_desc(block_k=128)) == sa.SA_ERR_UNSUPPORTED
+    assert call([0.1], desc=_desc(block_k=32)) == sa.SA_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("lam,n,m,sink,recent,code", [
@@ -199,7 +200,7 @@ def test_skip_nm_rejects(lam, n, m, sink, recent, code):
     assert got == getattr(sa, "SA_ERR_" + code)
     assert f(None, FAKE, FAKE, FAKE, FAKE, 0.1, 2, 4, 0, 0, None, None, None, None, None, None,
              None) == sa.SA_ERR_NULL
-    d64 = _desc(block_k=128)
+    d64 = _desc(block_k=32)
     assert f(ctypes.byref(d64), FAKE, FAKE, FAKE, FAKE, 0.1, 2, 4, 0, 0, None, None, None, None,
              None, None, None) == sa.SA_ERR_UNSUPPORTED
 
@@ -314,3 +315,32 @@ def test_binding_checks_route_sizes():
     with pytest.raises(ValueError, match="k_mean must hold"):
         sa.sa_proxy_block_sparse_fwd(q, k, k, _bf(1, 2, 4, 64), _bf(1, 2, 5, 64), i32(6),
                                      i32(6, 5), i32(6, 1), 1, q, block_q=128, block_k=64)
+
+
+@pytest.mark.parametrize("gran", [-1, 2, 7])
+def test_skip_ex_rejects_bad_granularity(gran):
+    d = _desc()
+    assert sa.raw.sa_skip_softmax_fwd_ex(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0.1, gran, None,
+                                         None, None, None, None) == sa.SA_ERR_VALUE
+
+
+def test_skip_ex_shares_the_descriptor_checks():
+    d = _desc(block_k=32)
+    assert sa.raw.sa_skip_softmax_fwd_ex(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0.1, 1, None,
+                                         None, None, None, None) == sa.SA_ERR_UNSUPPORTED
+    assert sa.raw.sa_skip_softmax_fwd_ex(ctypes.byref(_desc()), None, FAKE, FAKE, FAKE, 0.1, 1,
+                                         None, None, None, None, None) == sa.SA_ERR_NULL
+
+
+def test_binding_wave_granularity_output_sizes():
+    import torch
+    q, k = _bf(1, 100, 2, 64), _bf(1, 256, 2, 64)
+    o = _bf(1, 100, 2, 64)
+    # wave granularity: nR = ceil(100/32) = 4 blocks of 32 rows, nKT = 2 at block_k 128
+    with pytest.raises(ValueError, match="tile_state must hold"):
+        sa.sa_skip_softmax_fwd_ex(q, k, k, o, 0.5, "wave", block_k=128,
+                                  tile_state=torch.zeros(1, 2, 1, 2, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="must live on the GPU"):
+        sa.sa_skip_softmax_fwd_ex(q, k, k, o, 0.5, "wave", block_k=128,
+                                  tile_state=torch.zeros(1, 2, 4, 2, dtype=torch.uint8),
+                                  dbg_tile_rowmax=torch.zeros(1, 2, 4, 2, 32))

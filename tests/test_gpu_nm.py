@@ -118,3 +118,20 @@ def test_n_equals_m_is_dense_attention(n):
     allowed = np.tril(np.ones((S, S), bool))
     mask = np.unpackbits(g["bits"].view(np.uint8), axis=-1, bitorder="little")[..., :S].astype(bool)
     assert (mask == allowed[None, None]).all()
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (5, 8)])
+def test_block_k_128_same_result(n, m):
+    """The N:M rule does not use the key tile: block_k 128 gives the bits and output of 64."""
+    announce(f"nm block_k 128 {n}:{m}")
+    q, k, v = W.gen_llm(37, 1, 600, 2, 2, 128)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    outs = []
+    for bk in (64, 128):
+        o = torch.empty_like(qd)
+        bits = torch.empty((1, 2, 600, -(-600 // 32)), dtype=torch.int32, device="cuda")
+        sa.sa_nm_softmax_fwd(qd, kd, vd, o, n, m, 4, 128, causal=True, block_q=128, block_k=bk,
+                             dbg_keep_bits=bits)
+        torch.cuda.synchronize()
+        outs.append((from_dev_bf16(o), bits.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])

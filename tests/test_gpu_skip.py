@@ -24,36 +24,47 @@ pytestmark = pytest.mark.gpu
 sa = pytest.importorskip("sparse_attention_flash_amd")
 
 
-def run_gpu(q, k, v, causal, Br, lam, *, dbg=True, q_dev=None, k_dev=None, v_dev=None):
+def run_gpu(q, k, v, causal, Br, lam, *, dbg=True, q_dev=None, k_dev=None, v_dev=None, Bc=64,
+            gran="tile"):
+    """Runs the GPU with every export on.  Decision blocks are R = Br rows (tile granularity) or
+    R = 32 rows (wave granularity), so states and maxima are [B, Hq, ceil(Sq/R), nKT(, R)]."""
     B, Sq, Hq, D = q.shape
     Sk = k.shape[1]
-    nQT, nKT = -(-Sq // Br), -(-Sk // 64)
+    R = 32 if gran == "wave" else Br
+    nR, nKT = -(-Sq // R), -(-Sk // Bc)
     qd = q_dev if q_dev is not None else to_dev(q)
     kd = k_dev if k_dev is not None else to_dev(k)
     vd = v_dev if v_dev is not None else to_dev(v)
     o = torch.full((B, Sq, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
-    st = torch.full((B, Hq, nQT, nKT), 255, dtype=torch.uint8, device="cuda")
+    st = torch.full((B, Hq, nR, nKT), 255, dtype=torch.uint8, device="cuda")
     cnt = torch.zeros((B, Hq, 2), dtype=torch.int32, device="cuda")
     lse = torch.full((B, Hq, Sq), float("nan"), device="cuda")
-    rm = torch.empty((B, Hq, nQT, nKT, Br), device="cuda") if dbg else None
-    sa.sa_skip_softmax_fwd(qd, kd, vd, o, lam, causal=causal, block_q=Br, block_k=64,
-                           tile_state=st, head_counters=cnt, lse=lse, dbg_tile_rowmax=rm)
+    rm = torch.empty((B, Hq, nR, nKT, R), device="cuda") if dbg else None
+    kw = dict(causal=causal, block_q=Br, block_k=Bc, tile_state=st, head_counters=cnt, lse=lse,
+              dbg_tile_rowmax=rm)
+    if gran == "tile":
+        sa.sa_skip_softmax_fwd(qd, kd, vd, o, lam, **kw)
+    else:
+        sa.sa_skip_softmax_fwd_ex(qd, kd, vd, o, lam, gran, **kw)
     torch.cuda.synchronize()
     return dict(o=from_dev_bf16(o), st=st.cpu().numpy(), cnt=cnt.cpu().numpy(),
                 lse=lse.cpu().numpy(), rm=None if rm is None else rm.cpu().numpy())
 
 
-def check_case(q, k, v, causal, Br, lam, tag):
-    announce(f"skip {tag} lam={lam}")
+def check_case(q, k, v, causal, Br, lam, tag, *, Bc=64, gran="tile"):
+    """Wave granularity is checked against the oracle's tile rule on 32-row query tiles: each
+    32-row block has its own running max and its own decisions."""
+    announce(f"skip {tag} lam={lam} Bc={Bc} gran={gran}")
     D = q.shape[-1]
     scale = 1 / math.sqrt(D)
-    g = run_gpu(q, k, v, causal, Br, lam)
+    g = run_gpu(q, k, v, causal, Br, lam, Bc=Bc, gran=gran)
     st = g["st"]
     assert set(np.unique(st)) <= {0, 1, 2}
     # counters = histogram of tile_state
     assert (g["cnt"][..., 0] == (st != 2).sum(-1).sum(-1)).all()
     assert (g["cnt"][..., 1] == (st == 1).sum(-1).sum(-1)).all()
-    kw = dict(causal=causal, block_q=Br, block_k=64, scale=scale, lam=lam)
+    R = 32 if gran == "wave" else Br
+    kw = dict(causal=causal, block_q=R, block_k=Bc, scale=scale, lam=lam)
     # replay: decisions bit-exact given the GPU's maxima
     _, _, st_replay, _ = oracle.skip_softmax(q, k, v, mode=1, rowmax_in=g["rm"], **kw)
     assert np.array_equal(st_replay, st), "replayed decisions differ from the GPU's"
@@ -167,3 +178,115 @@ def test_counters_accumulate_and_stream_order():
     s.synchronize()
     one = run_gpu(q, k, v, True, 128, 1.0, dbg=False)["cnt"]
     assert np.array_equal(cnt.cpu().numpy(), 3 * one)
+
+
+# ---- 128-key decision tiles: two 64-key steps decided together ---------------------------------
+
+def late_keeps(q, k, causal, Br, lam, st128):
+    """Kept 128-key tiles whose first 64 keys alone are negligible against the running max before
+    the tile (the tile is kept only through its second half: the kernel then fetches the first
+    half's V late).  Computed in float64 from the oracle's 64-key maxima, to show the path runs."""
+    D = q.shape[-1]
+    _, _, _, rm64 = oracle.skip_softmax(q, k, k, causal=causal, block_q=Br, block_k=64,
+                                        scale=1 / math.sqrt(D), lam=0.0)
+    L = math.log2(lam) if lam > 0 else -math.inf
+    B, H, nQT, nKT128 = st128.shape
+    nKT64 = rm64.shape[3]
+    Sq = q.shape[1]
+    count = 0
+    for b in range(B):
+        for h in range(H):
+            for i in range(nQT):
+                nr = min(Br, Sq - i * Br)
+                m = np.full(nr, -np.inf)
+                for j in range(nKT128):
+                    if st128[b, h, i, j] != 0:
+                        continue
+                    a = rm64[b, h, i, 2 * j, :nr]
+                    bm = rm64[b, h, i, 2 * j + 1, :nr] if 2 * j + 1 < nKT64 else np.full(nr, -np.inf)
+                    if (a < m + L).all():
+                        count += 1
+                    m = np.maximum(m, np.maximum(a, bm))
+    return count
+
+
+@pytest.mark.parametrize("shape", [
+    # (B, Sq, Sk, Hq, Hkv, D, causal, Br)
+    (1, 256, 256, 2, 2, 64, False, 64),      # the small case at the pages' bc = 128
+    (1, 1000, 1000, 4, 2, 128, True, 64),    # causal with Br 64: the last 128-key tile of odd
+                                             # query tiles holds one 64-key step
+    (1, 1000, 1000, 2, 2, 128, True, 128),   # br = bc = 128
+    (1, 200, 300, 2, 2, 128, False, 128),    # last 128-key tile is 44 keys (one step)
+    (2, 130, 130, 4, 1, 64, True, 128),      # 2-row last query tile, GQA 4:1
+])
+@pytest.mark.parametrize("lam", [0.0, 0.5, 1.0, 1.5, 3.0, 1e30])
+def test_block_k_128(shape, lam):
+    B, Sq, Sk, Hq, Hkv, D, causal, Br = shape
+    if causal:
+        q, k, v = W.gen_llm(61, B, Sq, Hq, Hkv, D)
+    else:
+        q, k, v = W.gen_iid(61, B, Sq, Sk, Hq, Hkv, D)
+    st, _, _ = check_case(q, k, v, causal, Br, lam, f"bk128 {shape}", Bc=128)
+    if lam == 0.0:
+        assert (st != 1).all()
+    if lam == 1e30:
+        assert (st[..., 0] == 0).all()
+
+
+def test_block_k_128_late_keeps_happen():
+    """The sweep above runs the late-keep path (tiles kept through their second half only)."""
+    q, k, v = W.gen_iid(61, 1, 256, 256, 2, 2, 64)
+    seen = 0
+    for lam in (1.0, 1.5, 3.0):
+        g = run_gpu(q, k, v, False, 64, lam, dbg=False, Bc=128)
+        seen += late_keeps(q, k, False, 64, lam, g["st"])
+    assert seen > 0
+
+
+def test_block_k_128_llm_causal_gqa():
+    """The causal GQA prefill generator at a reduced size with the pages' br = bc = 128."""
+    q, k, v = W.gen_llm(2, 1, 2048, 8, 2, 128)
+    st, _, _ = check_case(q, k, v, True, 128, 1.5127145, "llm_causal_gqa_s2048", Bc=128)
+    assert 0 < (st == 1).sum() < (st != 2).sum()
+
+
+# ---- wave granularity: each 32-row wavefront decides alone ----------------------------------------
+
+@pytest.mark.parametrize("shape", [
+    # (B, Sq, Sk, Hq, Hkv, D, causal, Br)
+    (1, 256, 256, 2, 2, 64, False, 64),
+    (1, 1000, 1000, 4, 2, 128, True, 128),   # causal: the waves of a tile visit different tiles
+    (1, 200, 300, 2, 2, 128, False, 128),    # ragged: a wave with 8 rows, a wave with none
+    (2, 130, 130, 4, 1, 64, True, 64),
+])
+@pytest.mark.parametrize("Bc", [64, 128])
+@pytest.mark.parametrize("lam", [0.0, 0.5, 1.0, 3.0])
+def test_wave_granularity(shape, Bc, lam):
+    B, Sq, Sk, Hq, Hkv, D, causal, Br = shape
+    if causal:
+        q, k, v = W.gen_llm(62, B, Sq, Hq, Hkv, D)
+    else:
+        q, k, v = W.gen_iid(62, B, Sq, Sk, Hq, Hkv, D)
+    st, _, _ = check_case(q, k, v, causal, Br, lam, f"wave {shape}", Bc=Bc, gran="wave")
+    if lam == 0.0:
+        assert (st != 1).all()
+
+
+@pytest.mark.parametrize("lam", [0.3, 0.6, 1.0])
+def test_wave_sparsity_at_least_tile_sparsity(lam):
+    """For lambda <= 1 a skipped tile never raises the running max, so every row's running max is
+    the dense prefix max under both granularities: a tile skipped by the whole query tile is
+    skipped by each of its waves, and the wave sparsity is at least the tile sparsity."""
+    announce(f"wave vs tile sparsity lam={lam}")
+    q, k, v = W.gen_llm(63, 1, 2048, 4, 4, 128)
+    t = run_gpu(q, k, v, True, 128, lam, dbg=False)
+    w = run_gpu(q, k, v, True, 128, lam, dbg=False, gran="wave")
+    ts, ws = t["st"], w["st"]              # [1, H, 16, nKT] and [1, H, 64, nKT]
+    tile_skip = np.repeat(ts == 1, 4, axis=2)
+    # skipped by each wave that visits it (a wave below the diagonal may not visit it at all)
+    assert (ws[tile_skip] != 0).all()
+    # and over the (wave, tile) pairs a wave visits, at least as many skips
+    vis = ws != 2
+    assert (ws[vis] == 1).sum() >= tile_skip[vis].sum()
+    if lam >= 0.6:
+        assert (ws[vis] == 1).sum() > tile_skip[vis].sum()   # the finer rule skips more

@@ -26,10 +26,10 @@ pytestmark = pytest.mark.gpu
 sa = pytest.importorskip("sparse_attention_flash_amd")
 
 
-def run_gpu(q, k, v, causal, Br, lam, n, m, sink, recent):
+def run_gpu(q, k, v, causal, Br, lam, n, m, sink, recent, Bc=64):
     B, Sq, Hq, D = q.shape
     Sk = k.shape[1]
-    nQT, nKT, Wd = -(-Sq // Br), -(-Sk // 64), -(-Sk // 32)
+    nQT, nKT, Wd = -(-Sq // Br), -(-Sk // Bc), -(-Sk // 32)
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
     o = torch.full((B, Sq, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
     st = torch.full((B, Hq, nQT, nKT), 255, dtype=torch.uint8, device="cuda")
@@ -39,12 +39,12 @@ def run_gpu(q, k, v, causal, Br, lam, n, m, sink, recent):
     bits = torch.full((B, Hq, Sq, Wd), -1, dtype=torch.int32, device="cuda")
     sc = torch.full((B, Hq, Sq, Sk), float("nan"), device="cuda")
     sa.sa_skip_nm_softmax_fwd(qd, kd, vd, o, lam, n, m, sink, recent, causal=causal, block_q=Br,
-                              tile_state=st, head_counters=cnt, lse=lse, dbg_tile_rowmax=rm,
+                              block_k=Bc, tile_state=st, head_counters=cnt, lse=lse, dbg_tile_rowmax=rm,
                               dbg_keep_bits=bits, dbg_scores=sc)
     # the two separate kernels on the same inputs
     st_skip = torch.full_like(st, 255)
     sa.sa_skip_softmax_fwd(qd, kd, vd, torch.empty_like(o), lam, causal=causal, block_q=Br,
-                           tile_state=st_skip)
+                           block_k=Bc, tile_state=st_skip)
     bits_nm = torch.full_like(bits, -1)
     sa.sa_nm_softmax_fwd(qd, kd, vd, torch.empty_like(o), n, m, sink, recent, causal=causal,
                          block_q=Br, dbg_keep_bits=bits_nm)
@@ -55,16 +55,16 @@ def run_gpu(q, k, v, causal, Br, lam, n, m, sink, recent):
                 st_skip=st_skip.cpu().numpy(), bits_nm=bits_nm.cpu().numpy().view(np.uint32))
 
 
-def check(q, k, v, causal, Br, lam, n, m, sink, recent, tag):
-    announce(f"skip+nm {tag} lam={lam} {n}:{m} sink={sink} recent={recent}")
+def check(q, k, v, causal, Br, lam, n, m, sink, recent, tag, Bc=64):
+    announce(f"skip+nm {tag} lam={lam} {n}:{m} sink={sink} recent={recent} Bc={Bc}")
     D = q.shape[-1]
-    g = run_gpu(q, k, v, causal, Br, lam, n, m, sink, recent)
+    g = run_gpu(q, k, v, causal, Br, lam, n, m, sink, recent, Bc)
     st = g["st"]
     assert np.array_equal(st, g["st_skip"]), "tile states differ from the skip kernel's"
     assert np.array_equal(g["bits"], g["bits_nm"]), "keep bits differ from the N:M kernel's"
     assert (g["cnt"][..., 0] == (st != 2).sum(-1).sum(-1)).all()
     assert (g["cnt"][..., 1] == (st == 1).sum(-1).sum(-1)).all()
-    kw = dict(causal=causal, block_q=Br, block_k=64, scale=1 / math.sqrt(D), lam=lam, n=n, m=m,
+    kw = dict(causal=causal, block_q=Br, block_k=Bc, scale=1 / math.sqrt(D), lam=lam, n=n, m=m,
               sink=sink, recent=recent)
     _, _, st_r, _, kb_r = oracle.skip_nm_softmax(q, k, v, mode=1, rowmax_in=g["rm"],
                                                  scores_in=g["sc"], **kw)
@@ -114,3 +114,14 @@ def test_video_non_causal():
     q, k, v = W.gen_video(23, 1, 2, 128, grid=(3, 10, 20))
     st = check(q, k, v, False, 128, 0.378, 2, 4, 0, 0, "video grid 3x10x20")
     assert (st == 1).sum() > 0
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (3, 8)])
+@pytest.mark.parametrize("lam", [0.0, 1.0, 3.0])
+@pytest.mark.parametrize("Br", [64, 128])
+def test_block_k_128(n, m, lam, Br):
+    """The pages' bc = 128: 128-key decision tiles over the N:M-masked logits."""
+    q, k, v = W.gen_llm(24, 1, 1000, 4, 2, 128)
+    st = check(q, k, v, True, Br, lam, n, m, 4, 128, "llm causal gqa s1000", Bc=128)
+    if lam >= 3.0:
+        assert (st == 1).sum() > 0
