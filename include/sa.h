@@ -47,7 +47,8 @@ typedef enum {
   SA_ERR_UNSUPPORTED = 3, /* head_dim / tile / (n, m) / causal-proxy combination not implemented */
   SA_ERR_ALIGN = 4,       /* non-16-byte-aligned pointer or stride */
   SA_ERR_VALUE = 5,       /* bad scalar: lambda, softmax_scale, calibration inputs, sink/recent */
-  SA_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+  SA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
+  SA_ERR_SCRATCH = 7      /* needs more scratch than the fixed device buffer holds (noalloc) */
 } sa_status;
 
 /* Human-readable name of a status code (static string). */
@@ -206,6 +207,29 @@ sa_status sa_skip_softmax_decode_fwd(const sa_attn_desc* desc, const void* q, co
                                      void* workspace, size_t workspace_bytes,
                                      uint8_t* tile_state, uint32_t* head_counters, float* lse,
                                      float* dbg_tile_rowmax, void* stream);
+
+/*
+ * Decode-phase skip-softmax forward that allocates nothing and takes no workspace: for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops, harnesses that forbid
+ * allocation).  Same arguments, kernels and results as sa_skip_softmax_decode_fwd without the
+ * workspace pair: the workspace lives in a fixed device array inside the library, one copy per GPU,
+ * SA_DECODE_SCRATCH_BYTES long and held until the process ends.
+ *
+ *   - A call whose sa_skip_softmax_decode_workspace size exceeds SA_DECODE_SCRATCH_BYTES returns
+ *     SA_ERR_SCRATCH (nothing enqueued).
+ *   - The first call on a device looks up that device's copy of the array (hipGetSymbolAddress,
+ *     with the device current); make one call before capturing a graph around later ones.
+ *   - Every call on a GPU shares that GPU's array, and it keeps the last call's contents: calls
+ *     that overlap on one GPU (on different streams, or from different threads) race and must be
+ *     serialised by the caller.  Nothing in the array needs clearing between calls (every region
+ *     is written before it is read).
+ */
+#define SA_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+sa_status sa_skip_softmax_decode_fwd_noalloc(const sa_attn_desc* desc, const void* q,
+                                             const void* k, const void* v, void* o, float lambda,
+                                             const int32_t* seqlens_k, int32_t num_splits,
+                                             uint8_t* tile_state, uint32_t* head_counters,
+                                             float* lse, float* dbg_tile_rowmax, void* stream);
 
 /*
  * Route preparation, the "plan" step of the block-sparse path (FlashInfer proxy description,

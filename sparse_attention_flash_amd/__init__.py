@@ -29,9 +29,11 @@ SA_SKIP_GRAN_TILE, SA_SKIP_GRAN_WAVE = 0, 1
 GRANULARITY = {"tile": SA_SKIP_GRAN_TILE, "wave": SA_SKIP_GRAN_WAVE}
 WAVE_ROWS = 32   # decision rows at wave granularity
 
-SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_ALIGN, SA_ERR_VALUE, SA_ERR_HIP = range(7)
+(SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_ALIGN, SA_ERR_VALUE, SA_ERR_HIP,
+ SA_ERR_SCRATCH) = range(8)
 STATUS_NAMES = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_UNSUPPORTED",
-                4: "SA_ERR_ALIGN", 5: "SA_ERR_VALUE", 6: "SA_ERR_HIP"}
+                4: "SA_ERR_ALIGN", 5: "SA_ERR_VALUE", 6: "SA_ERR_HIP", 7: "SA_ERR_SCRATCH"}
+SA_DECODE_SCRATCH_BYTES = 32 << 20
 
 
 class sa_attn_desc(ctypes.Structure):
@@ -66,6 +68,9 @@ _lib.sa_skip_softmax_decode_workspace.restype = ctypes.c_int
 _lib.sa_skip_softmax_decode_fwd.argtypes = [_DESC, _P, _P, _P, _P, _F, _P, _I32, _P, ctypes.c_size_t,
                                             _P, _P, _P, _P, _P]
 _lib.sa_skip_softmax_decode_fwd.restype = ctypes.c_int
+_lib.sa_skip_softmax_decode_fwd_noalloc.argtypes = [_DESC, _P, _P, _P, _P, _F, _P, _I32, _P, _P,
+                                                    _P, _P, _P]
+_lib.sa_skip_softmax_decode_fwd_noalloc.restype = ctypes.c_int
 _lib.sa_bitmask_route_prep.argtypes = [_DESC, _P, _P, _P, _P, _P]
 _lib.sa_bitmask_route_prep.restype = ctypes.c_int
 _lib.sa_bsr_route_prep.argtypes = [_DESC, _P, _P, ctypes.c_int64, _P, _P, _P, _P, _P]
@@ -301,6 +306,25 @@ def _route_outputs(d, n_exact, exact_idx, proxy_keep):
     _need(n_exact, "n_exact", rows, _U32)
     _need(exact_idx, "exact_idx", rows * nKB, _U32)
     _need(proxy_keep, "proxy_keep", rows * (-(-nKB // 32)), _U32)
+
+
+def sa_skip_softmax_decode_fwd_noalloc(q, k, v, o, lam, *, block_k=64, seqlens_k=None,
+                                       num_splits=0, scale=None, tile_state=None,
+                                       head_counters=None, lse=None, dbg_tile_rowmax=None,
+                                       stream=None):
+    """sa_skip_softmax_decode_fwd with its workspace in the library's fixed device array (no
+    allocation anywhere; calls that overlap on one GPU race, see sa.h)."""
+    d = make_desc(q, k, v, o, block_q=64, block_k=block_k, scale=scale)
+    BH, nKT = d.batch * d.heads_q, -(-d.seqlen_k // max(1, d.block_k))
+    _need(seqlens_k, "seqlens_k", d.batch, (torch.int32,))
+    _need(tile_state, "tile_state", BH * nKT, _U8)
+    _need(head_counters, "head_counters", BH * 2, _U32)
+    _need(lse, "lse", BH, _F32)
+    _need(dbg_tile_rowmax, "dbg_tile_rowmax", BH * nKT, _F32)
+    _check(_lib.sa_skip_softmax_decode_fwd_noalloc(
+        ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), float(lam), _ptr(seqlens_k),
+        int(num_splits), _ptr(tile_state), _ptr(head_counters), _ptr(lse), _ptr(dbg_tile_rowmax),
+        _stream(stream)), "sa_skip_softmax_decode_fwd_noalloc")
 
 
 def sa_bitmask_route_prep(bitmask, n_exact, exact_idx, proxy_keep, *, batch, heads_kv, seqlen_q,

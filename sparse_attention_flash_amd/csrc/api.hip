@@ -12,6 +12,9 @@
 #include "kernels.h"
 #include "sa.h"
 
+static_assert(sa::kDecodeScratchBytes == SA_DECODE_SCRATCH_BYTES,
+              "the scratch size sa.h states is the array's");
+
 namespace {
 
 constexpr double kLog2eD = 1.4426950408889634074;
@@ -143,6 +146,31 @@ sa_status plan_decode(const sa_attn_desc* d, float lambda, int32_t num_splits, D
 
 
 
+// Enqueue the three decode kernels over the workspace at `ws` laid out by the plan (every region
+// is written before it is read, so nothing needs clearing).
+sa_status decode_run(const sa_attn_desc& d, const DecodePlan& p, const void* q, const void* k,
+                     const void* v, void* o, float lambda, const int32_t* seqlens_k, char* ws,
+                     uint8_t* tile_state, uint32_t* head_counters, float* lse,
+                     float* dbg_tile_rowmax, void* stream) {
+  sa::DecodeArgs a{};
+  a.g = geometry(&d, q, k, v, o);
+  a.L32 = lambda == 0.f ? -INFINITY : (float)std::log2((double)lambda);
+  a.seqlens_k = seqlens_k;
+  a.block_k = d.block_k;
+  a.nKT = p.nKT;
+  a.nsplit = p.nsplit;
+  a.tiles_per_split = p.tps;
+  a.scores = reinterpret_cast<float*>(ws + p.off_scores);
+  a.tmax = dbg_tile_rowmax != nullptr ? dbg_tile_rowmax : reinterpret_cast<float*>(ws + p.off_tmax);
+  a.part_m = reinterpret_cast<float*>(ws + p.off_pm);
+  a.part_l = reinterpret_cast<float*>(ws + p.off_pl);
+  a.part_o = reinterpret_cast<float*>(ws + p.off_po);
+  a.tile_state = tile_state;
+  a.counters = head_counters;
+  a.lse = lse;
+  return from_hip(sa::launch_skip_decode(a, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -156,6 +184,8 @@ const char* sa_status_str(sa_status status) {
     case SA_ERR_ALIGN: return "SA_ERR_ALIGN: pointer or stride not 16-byte aligned";
     case SA_ERR_VALUE: return "SA_ERR_VALUE: invalid scalar argument";
     case SA_ERR_HIP: return "SA_ERR_HIP: the HIP runtime reported an error";
+    case SA_ERR_SCRATCH:
+      return "SA_ERR_SCRATCH: the call needs more device scratch than the fixed buffer holds";
   }
   return "unknown sa_status";
 }
@@ -271,24 +301,28 @@ sa_status sa_skip_softmax_decode_fwd(const sa_attn_desc* desc, const void* q, co
   if (workspace == nullptr) return SA_ERR_NULL;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return SA_ERR_ALIGN;
   if (workspace_bytes < p.bytes) return SA_ERR_SHAPE;
-  sa::DecodeArgs a{};
-  a.g = geometry(&d, q, k, v, o);
-  a.L32 = lambda == 0.f ? -INFINITY : (float)std::log2((double)lambda);
-  a.seqlens_k = seqlens_k;
-  a.block_k = d.block_k;
-  a.nKT = p.nKT;
-  a.nsplit = p.nsplit;
-  a.tiles_per_split = p.tps;
-  char* ws = static_cast<char*>(workspace);
-  a.scores = reinterpret_cast<float*>(ws + p.off_scores);
-  a.tmax = dbg_tile_rowmax != nullptr ? dbg_tile_rowmax : reinterpret_cast<float*>(ws + p.off_tmax);
-  a.part_m = reinterpret_cast<float*>(ws + p.off_pm);
-  a.part_l = reinterpret_cast<float*>(ws + p.off_pl);
-  a.part_o = reinterpret_cast<float*>(ws + p.off_po);
-  a.tile_state = tile_state;
-  a.counters = head_counters;
-  a.lse = lse;
-  return from_hip(sa::launch_skip_decode(a, (hipStream_t)stream));
+  return decode_run(d, p, q, k, v, o, lambda, seqlens_k, static_cast<char*>(workspace), tile_state,
+                    head_counters, lse, dbg_tile_rowmax, stream);
+}
+
+sa_status sa_skip_softmax_decode_fwd_noalloc(const sa_attn_desc* desc, const void* q,
+                                             const void* k, const void* v, void* o, float lambda,
+                                             const int32_t* seqlens_k, int32_t num_splits,
+                                             uint8_t* tile_state, uint32_t* head_counters,
+                                             float* lse, float* dbg_tile_rowmax, void* stream) {
+  if (desc == nullptr) return SA_ERR_NULL;
+  sa_attn_desc d = *desc;
+  d.block_q = 64;
+  sa_status st = check_attention(&d, q, k, v, o);
+  if (st != SA_OK) return st;
+  DecodePlan p;
+  st = plan_decode(&d, lambda, num_splits, &p);
+  if (st != SA_OK) return st;
+  if (p.bytes > sa::kDecodeScratchBytes) return SA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (sa::decode_scratch(&ws) != hipSuccess) return SA_ERR_HIP;
+  return decode_run(d, p, q, k, v, o, lambda, seqlens_k, static_cast<char*>(ws), tile_state,
+                    head_counters, lse, dbg_tile_rowmax, stream);
 }
 
 sa_status sa_bitmask_route_prep(const sa_attn_desc* desc, const uint32_t* bitmask,

@@ -24,10 +24,47 @@
 //                     heads into LDS (r = the split's max over its kept tiles, so no rescaling),
 //                     and the key-row lanes accumulate P.V from it;
 //   3 decode_combine  the splits' (r, l, O) merged into O and the natural-log LSE.
+#include <atomic>
+#include <mutex>
+
 #include "kernels.h"
 #include "tile_core.h"
 
+// The allocation-free decode entry point keeps its workspace here (scores, tile maxima, split
+// partials).  Host code never uses this name as an address: it is a host-side stand-in for the
+// device symbol, so every kernel argument, copy or fill takes the pointer decode_scratch() looks
+// up on the current device instead.
+static __device__ __attribute__((aligned(256))) char scratch[sa::kDecodeScratchBytes];
+
 namespace sa {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // first call on this device (with it current): the device address of its copy of the array
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 namespace {
 
 constexpr int kDecWaves = 4;

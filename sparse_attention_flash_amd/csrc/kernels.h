@@ -107,6 +107,12 @@ hipError_t launch_skip_softmax(const SkipArgs& a, hipStream_t stream);
 hipError_t launch_nm_softmax(const NmArgs& a, hipStream_t stream);
 hipError_t launch_skip_nm_softmax(const SkipNmArgs& a, hipStream_t stream);
 hipError_t launch_skip_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Device scratch of the allocation-free decode entry point: a fixed file-scope device array (one
+// copy per GPU, held until the process ends).  decode_scratch() returns the current device's
+// address of it, looked up once per device.
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_route_prep(const RouteArgs& a, hipStream_t stream);
 hipError_t launch_bsr_route_prep(const BsrRouteArgs& a, hipStream_t stream);
 hipError_t launch_proxy(const ProxyArgs& a, hipStream_t stream);

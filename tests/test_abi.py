@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(7):
+    for code in range(8):
         assert sa.sa_status_str(code).startswith(sa.STATUS_NAMES[code])
 
 
@@ -344,3 +344,23 @@ def test_binding_wave_granularity_output_sizes():
         sa.sa_skip_softmax_fwd_ex(q, k, k, o, 0.5, "wave", block_k=128,
                                   tile_state=torch.zeros(1, 2, 4, 2, dtype=torch.uint8),
                                   dbg_tile_rowmax=torch.zeros(1, 2, 4, 2, 32))
+
+
+def test_decode_noalloc_rejects_on_the_host():
+    f = sa.raw.sa_skip_softmax_decode_fwd_noalloc
+    d = _desc(seqlen_q=1, seqlen_k=8192, heads_q=32, heads_kv=8, batch=16)
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 0.1, None, 0, None, None, None, None, None) == sa.SA_ERR_NULL
+    assert f(ctypes.byref(d), None, FAKE, FAKE, FAKE, 0.1, None, 0, None, None, None, None,
+             None) == sa.SA_ERR_NULL
+    assert f(ctypes.byref(_desc()), FAKE, FAKE, FAKE, FAKE, 0.1, None, 0, None, None, None, None,
+             None) == sa.SA_ERR_UNSUPPORTED                         # seqlen_q != 1
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, -1.0, None, 0, None, None, None, None,
+             None) == sa.SA_ERR_VALUE
+    # a workspace larger than the fixed buffer: 4x the decode workload's cache
+    big = _desc(seqlen_q=1, seqlen_k=4 * 8192, heads_q=32, heads_kv=8, batch=16)
+    need = ctypes.c_size_t()
+    assert sa.raw.sa_skip_softmax_decode_workspace(ctypes.byref(big), ctypes.c_float(0.1), 0,
+                                                   ctypes.byref(need), None) == sa.SA_OK
+    assert need.value > sa.SA_DECODE_SCRATCH_BYTES
+    assert f(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, 0.1, None, 0, None, None, None, None,
+             None) == sa.SA_ERR_SCRATCH
