@@ -94,6 +94,17 @@ __device__ __forceinline__ DecUnit dec_unit(const DecodeArgs& a) {
   return u;
 }
 
+// Elements r of a lane's s[kb] whose key 32*kb + (r/4)*8 + r%4 (+ 4*(lane/32), in lim) is at
+// or past lim become -inf.  Here the MFMA rows are the K rows in order (no key permutation: the
+// rows come straight from global memory), so element r holds row (r/4)*8 + 4*(lane/32) + r%4.
+__device__ __forceinline__ void mask_rows(f32x16& s, int kb, int lim) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+    s[r] = select_neg_inf(s[r], (uint32_t)((lim - 1 - off) >> 31));
+  }
+}
+
 // ---- 1: scores and tile maxima --------------------------------------------------------------------
 // S^T = K.Q^T on v_mfma_f32_32x32x16_bf16, one 32-key block at a time: A = 32 K rows (lane l: key
 // l%32, the 8 values at d = 16ks + 8(l/32)), B = Q^T with the G heads as columns (columns past G
@@ -168,7 +179,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_scores(DecodeArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       // keys past the sequence: -inf (their rows read as zeros)
-      mask_block(s[kb], kb, u.len - key0 - 4 * hl);
+      mask_rows(s[kb], kb, u.len - key0 - 4 * hl);
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
       if (col < GM) {

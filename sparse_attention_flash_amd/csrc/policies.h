@@ -107,15 +107,15 @@ struct KeyTiles {
                    k_stride_b, v_stride_b};
   }
 
-  // key = k0 + 4*h + off(kb, r) with off a compile-time constant; masked when off >= lim
+  // key = k0 + 8*h + elem_key(kb, r), a compile-time offset; masked when it reaches lim
   __device__ __forceinline__ void mask(int j, f32x16 (&s)[2][QB], int) const {
     const int k0 = j * kKeysPerTile;
     if (!((k0 + kKeysPerTile > Sk) || (causal && k0 + kKeysPerTile - 1 > wrow0))) return;
-    const int klim = Sk - k0 - 4 * h;
+    const int klim = Sk - k0 - 8 * h;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       int lim = klim;
-      if (causal) lim = min(lim, wrow0 + qb * 32 + r32 - k0 - 4 * h + 1);
+      if (causal) lim = min(lim, wrow0 + qb * 32 + r32 - k0 - 8 * h + 1);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) mask_block(s[kb][qb], kb, lim);
     }
@@ -235,58 +235,46 @@ struct SkipDecision : KeyTiles<QB> {
 };
 
 // ---- the N:M rule ---------------------------------------------------------------------------------
-// In the S^T register layout a lane holds, for one query, keys 8g + 4h + {0..3} in elements
-// 4g..4g+3 (h = lane/32), so an M = 4 group is four consecutive elements of one lane and an M = 8
-// group is those four plus the same four elements of lane ^ 32 (one v_permlane32_swap).  Dropped
-// keys get weight 0 in P.  The running max needs no change: the group maximum always survives
-// (rank 0 < N), so the max over kept keys equals the max over allowed keys -- which is also why
-// the skip rule may be decided on the unfiltered tile maxima.
+// In the S^T register layout (tile_core.h, "Key order") element r of a lane's block kb holds, for
+// one query, key 32*kb + 16*(r/8) + 8*h + r%8 (h = lane/32): every run of 8 elements r = 8c..8c+7
+// is 8 consecutive keys.  A group of M = 4 consecutive keys is elements 4g..4g+3 and a group of
+// M = 8 is elements 8c..8c+7, both inside one lane, with keys increasing with the element index.
+// Dropped keys get weight 0 in P.  The running max needs no change: the group maximum always
+// survives (rank 0 < N), so the max over kept keys equals the max over allowed keys -- which is
+// also why the skip rule may be decided on the unfiltered tile maxima.
 
 // 1 when d < 0, else 0, for d the fp32 difference of two finite scores normalised by "+ 0.0f"
 // (so that equal scores give +0): the sign bit, read without a compare (a compare per pair would
 // park a lane mask in SGPRs).
 __device__ __forceinline__ int neg01(float d) { return (int)(__float_as_uint(d + 0.0f) >> 31); }
 
-// rank[i] = number of group members that beat own[i]: a higher score, or an equal score at a lower
-// key index.  own[0..3] are this lane's four keys in ascending key order; for M = 8, oth[0..3] are
-// the lane ^ 32 half of the group, whose keys all come after ours when own_first is true.  Scores
-// are finite here (masked keys enter as -FLT_MAX, which still ties only with other masked keys).
+// rank[i] = number of group members that beat x[i]: a higher score, or an equal score at a lower
+// key index.  x[0..M-1] are the group's scores in ascending key order; they are finite (masked
+// keys enter as -FLT_MAX, which ties only with other masked keys and ranks below every score).
 template <int M>
-__device__ __forceinline__ void group_ranks(const float (&own)[4], const float (&oth)[4],
-                                            bool own_first, int (&rank)[4]) {
+__device__ __forceinline__ void group_ranks(const float (&x)[M], int (&rank)[M]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) rank[i] = 0;
+  for (int i = 0; i < M; ++i) rank[i] = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < M; ++i)
 #pragma unroll
-    for (int j = i + 1; j < 4; ++j) {
-      // j comes after i: j beats i iff own[j] > own[i], otherwise i beats j
-      const int jgt = neg01(own[i] - own[j]);
+    for (int j = i + 1; j < M; ++j) {
+      // j comes after i: j beats i iff x[j] > x[i], otherwise i beats j
+      const int jgt = neg01(x[i] - x[j]);
       rank[i] += jgt;
       rank[j] += 1 - jgt;
     }
-  if constexpr (M == 8) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // other half after ours: it beats own[i] iff strictly greater; before ours: iff >=
-        const int gt = neg01(own[i] - oth[j]);   // oth[j] > own[i]
-        const int lt = neg01(oth[j] - own[i]);   // oth[j] < own[i]
-        rank[i] += own_first ? gt : 1 - lt;
-      }
-  }
 }
 
 // This lane's 32 keys of a 64-key tile, bit b = kb*16 + r, sit at key offsets
-// p(b) = kb*32 + (r/4)*8 + 4h + r%4, which increase with b: the keys with offset < T are the
+// p(b) = kb*32 + 16*(r/8) + 8h + r%8, which increase with b: the keys with offset < T are the
 // low bits, as many as there are such offsets.
 __device__ __forceinline__ uint32_t bits_below(int T, int h) {
   int cnt = 0;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) cnt += min(max(T - (kb * 32 + q * 8 + 4 * h), 0), 4);
+    for (int c = 0; c < 2; ++c) cnt += min(max(T - (kb * 32 + c * 16 + 8 * h), 0), 8);
   return cnt >= 32 ? 0xFFFFFFFFu : ((1u << cnt) - 1u);
 }
 
@@ -294,6 +282,7 @@ template <int NW, int QB, int M>
 struct NmFilter {
   static constexpr int RW = 32 * QB;
   static constexpr int BR = NW * RW;
+  static constexpr int kGroups = 16 / M;   // groups per block of 16 elements
   int n, sink, recent, W;
   uint32_t* keep_bits;
   float* scores;
@@ -311,55 +300,54 @@ struct NmFilter {
     row_base = ((int64_t)u.b * a.g.Hq + u.hq) * a.g.Sq;
   }
 
-  // The rank path: a key is dropped (-inf) unless it is among the top n of its group or lies in
-  // the sink/recent window.  The ranks are sign-bit arithmetic per element, exact for ties; the
-  // windows are key ranges, turned into bit ranges (bits_below) on the few tiles per row that
-  // touch them.  Masked keys are -inf already and stay so.  Each group is decided and applied
-  // before the next is ranked (for M = 8 the other half of a group sits in lane ^ 32, whose
-  // elements of that group are untouched until the same step).
+  // some row of this wave has a sink or recent-window key in the tile
+  __device__ __forceinline__ bool dense_tile(const KeyTiles<QB>& kt, int k0) const {
+    return k0 < sink ||
+           (recent > 0 && k0 <= kt.wrow0 + RW - 1 && k0 + kKeysPerTile - 1 > kt.wrow0 - recent);
+  }
+
+  // The window bits of query block qb (key < sink, or row - recent < key <= row), as bits
+  // b = kb*16 + r of this lane's elements.
+  __device__ __forceinline__ uint32_t window(const KeyTiles<QB>& kt, int k0, int qb) const {
+    const int row = kt.wrow0 + qb * 32 + kt.r32;
+    uint32_t win = bits_below(sink - k0, kt.h);
+    if (recent > 0)
+      win |= bits_below(row - k0 + 1, kt.h) & ~bits_below(row - recent - k0 + 1, kt.h);
+    return win;
+  }
+
+  // The exact rank pass: a key is dropped (-inf) unless it is among the top n of its group or lies
+  // in the sink/recent window.  The ranks are sign-bit arithmetic per pair, exact for ties.
+  // Masked keys are -inf already and stay so.
   __device__ __forceinline__ void rank_apply(const KeyTiles<QB>& kt, int j, f32x16 (&s)[2][QB],
-                                             int lane) const {
+                                             int) const {
     const int k0 = j * kKeysPerTile;
-    const int wrow0 = kt.wrow0, h = kt.h;
     const bool any_dense = dense_tile(kt, k0);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const int row = wrow0 + qb * 32 + kt.r32;
-      uint32_t win = 0u;
-      if (any_dense) {   // key < sink, or row - recent < key <= row
-        win = bits_below(sink - k0, h);
-        if (recent > 0) win |= bits_below(row - k0 + 1, h) & ~bits_below(row - recent - k0 + 1, h);
-      }
+      const uint32_t win = any_dense ? window(kt, k0, qb) : 0u;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          float own[4], oth[4];
+        for (int g = 0; g < kGroups; ++g) {
+          float x[M];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            own[e] = fmaxf(s[kb][qb][4 * gi + e], -3.402823466e38f);   // masked: finite sentinel
-            oth[e] = own[e];
-            if constexpr (M == 8) oth[e] = other_half(own[e], lane);
-          }
-          int rank[4];
-          group_ranks<M>(own, oth, h == 0, rank);
+          for (int e = 0; e < M; ++e)
+            x[e] = fmaxf(s[kb][qb][M * g + e], -3.402823466e38f);   // masked: finite sentinel
+          int rank[M];
+          group_ranks<M>(x, rank);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bool keep = rank[e] < n || ((win >> (kb * 16 + 4 * gi + e)) & 1u);
-            s[kb][qb][4 * gi + e] = keep ? s[kb][qb][4 * gi + e] : -INFINITY;
+          for (int e = 0; e < M; ++e) {
+            const int r = M * g + e;
+            const bool keep = rank[e] < n || ((win >> (kb * 16 + r)) & 1u);
+            s[kb][qb][r] = keep ? s[kb][qb][r] : -INFINITY;
           }
-          // one group at a time: the scheduler would otherwise interleave all eight groups'
+          // one group at a time: the scheduler would otherwise interleave all groups'
           // comparisons and run out of registers
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
-  }
-
-  // some row of this wave has a sink or recent-window key in the tile
-  __device__ __forceinline__ bool dense_tile(const KeyTiles<QB>& kt, int k0) const {
-    return k0 < sink ||
-           (recent > 0 && k0 <= kt.wrow0 + RW - 1 && k0 + kKeysPerTile - 1 > kt.wrow0 - recent);
   }
 
   // The N-th and (N+1)-th largest of a group of four, t and u.  With a <= b <= c the first three
@@ -410,90 +398,99 @@ struct NmFilter {
     return t;
   }
 
-  // Threshold pass (M = 8): the group's other four keys are the same elements of lane ^ 32.  Each
-  // lane sorts its four; one v_permlane32_swap per sorted value then gives every lane both the
-  // lower half's and the upper half's value, and the N-th and (N+1)-th largest of the eight are
-  // read from those two sorted lists (the K-th largest of a union does not depend on which list
-  // is which, so both lanes of a group find the same t and u); then as for M = 4.
-  template <int N>
-  static __device__ __forceinline__ void threshold_apply8(f32x16 (&s)[2][QB], bool& tie) {
+  // Keys of a group below its N-th largest t are dropped unless they lie in a window.  This keeps
+  // every key that reaches t, which is exactly the top N unless the (N+1)-th largest u equals t (a
+  // tie at the threshold, decided by the lower key index); such groups set `tie`.
+  template <bool kWin>
+  static __device__ __forceinline__ void drop_below(f32x16& v, int r0, int cnt, float t, float u,
+                                                    uint32_t win, bool& tie) {
+    tie = tie || (u == t && t != -INFINITY);
+#pragma unroll
+    for (int e = 0; e < cnt; ++e) {
+      const int r = r0 + e;
+      if constexpr (kWin) {
+        const bool keep = !(v[r] < t) || ((win >> r) & 1u);
+        v[r] = keep ? v[r] : -INFINITY;
+      } else {
+        v[r] = v[r] < t ? -INFINITY : v[r];
+      }
+    }
+  }
+
+  // Threshold pass.  M = 4: each group's N-th and (N+1)-th largest by the max3/med3/min3
+  // construction.  M = 8: the two halves of a group sorted, then the N-th and (N+1)-th largest of
+  // the union.  Window keys (kWin) are kept whatever their rank.
+  template <int N, bool kWin>
+  static __device__ __forceinline__ void threshold_apply(f32x16 (&s)[2][QB],
+                                                         const uint32_t (&win)[QB], bool& tie) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
+        for (int g = 0; g < kGroups; ++g) {
           f32x16& v = s[kb][qb];
-          float a[4], lo[4], hi[4];
-          sort4_desc(v[4 * gi], v[4 * gi + 1], v[4 * gi + 2], v[4 * gi + 3], a);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[e]),
-                                                             __float_as_uint(a[e]), false, false);
-            lo[e] = __uint_as_float(sw[0]);   // the value of lane l & 31
-            hi[e] = __uint_as_float(sw[1]);   // the value of lane l | 32
+          const uint32_t wb = kWin ? (win[qb] >> (kb * 16)) : 0u;
+          float t, u;
+          if constexpr (M == 4) {
+            nth_largest4<N>(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3], t, u);
+          } else {
+            float a[4], b[4];
+            sort4_desc(v[8 * g], v[8 * g + 1], v[8 * g + 2], v[8 * g + 3], a);
+            sort4_desc(v[8 * g + 4], v[8 * g + 5], v[8 * g + 6], v[8 * g + 7], b);
+            t = kth_largest8<N>(a, b);
+            u = kth_largest8<N + 1>(a, b);
           }
-          const float t = kth_largest8<N>(lo, hi), u = kth_largest8<N + 1>(lo, hi);
-          tie = tie || (u == t && t != -INFINITY);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[4 * gi + e] = v[4 * gi + e] < t ? -INFINITY : v[4 * gi + e];
+          drop_below<kWin>(v, M * g, M, t, u, wb, tie);
           __builtin_amdgcn_sched_barrier(0);   // one group at a time (register pressure)
         }
   }
 
-  // Threshold pass (M = 4): keys below their group's N-th largest t are dropped.  This keeps every
-  // key that reaches t, which is exactly the top N unless the (N+1)-th largest equals t (a tie at
-  // the threshold, decided by the lower key index); such groups set `tie`.
-  template <int N>
-  static __device__ __forceinline__ void threshold_apply(f32x16 (&s)[2][QB], bool& tie) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          f32x16& v = s[kb][qb];
-          float t, u;
-          nth_largest4<N>(v[4 * gi], v[4 * gi + 1], v[4 * gi + 2], v[4 * gi + 3], t, u);
-          tie = tie || (u == t && t != -INFINITY);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[4 * gi + e] = v[4 * gi + e] < t ? -INFINITY : v[4 * gi + e];
-          __builtin_amdgcn_sched_barrier(0);   // one group at a time (register pressure)
-        }
+  template <bool kWin>
+  __device__ __forceinline__ void threshold_n(f32x16 (&s)[2][QB], const uint32_t (&win)[QB],
+                                              bool& tie) const {
+    if constexpr (M == 4) {
+      switch (n) {
+        case 1: threshold_apply<1, kWin>(s, win, tie); break;
+        case 2: threshold_apply<2, kWin>(s, win, tie); break;
+        case 3: threshold_apply<3, kWin>(s, win, tie); break;
+        default: break;   // n >= M keeps every allowed key
+      }
+    } else {
+      switch (n) {
+        case 1: threshold_apply<1, kWin>(s, win, tie); break;
+        case 2: threshold_apply<2, kWin>(s, win, tie); break;
+        case 3: threshold_apply<3, kWin>(s, win, tie); break;
+        case 4: threshold_apply<4, kWin>(s, win, tie); break;
+        case 5: threshold_apply<5, kWin>(s, win, tie); break;
+        case 6: threshold_apply<6, kWin>(s, win, tie); break;
+        case 7: threshold_apply<7, kWin>(s, win, tie); break;
+        default: break;
+      }
+    }
   }
 
   // Drops the keys the rule does not keep by setting their scores to -inf (masked keys already
-  // are).  On a tile without window keys: the threshold pass, then, only if some group of the wave
-  // had a tie at its threshold, the rank pass over the result.  That is exact: the keys the
-  // threshold pass dropped lie below the N-th largest, so they are not in the top N either, and
-  // the rank pass ranks the surviving keys as it would rank them among all.  Tiles touching a
-  // window take the rank pass directly.
+  // are): the threshold pass, with the window bits on the tiles that touch a window, then, only if
+  // some group of the wave had a tie at its threshold, the rank pass over the result.  That is
+  // exact: the keys the threshold pass dropped lie below the N-th largest and outside the windows,
+  // so the rule drops them too, and the rank pass ranks the surviving keys as it would rank them
+  // among all.
   __device__ __forceinline__ void filter(const KeyTiles<QB>& kt, int j, f32x16 (&s)[2][QB],
                                          int lane) const {
     const int k0 = j * kKeysPerTile;
     if (scores != nullptr) export_scores(kt, k0, s);
-    bool exact = true;
-    if (!dense_tile(kt, k0)) {
-      bool tie = false;
-      if constexpr (M == 4) {
-        if (n == 1) threshold_apply<1>(s, tie);
-        else if (n == 2) threshold_apply<2>(s, tie);
-        else if (n == 3) threshold_apply<3>(s, tie);
-      } else {
-        switch (n) {
-          case 1: threshold_apply8<1>(s, tie); break;
-          case 2: threshold_apply8<2>(s, tie); break;
-          case 3: threshold_apply8<3>(s, tie); break;
-          case 4: threshold_apply8<4>(s, tie); break;
-          case 5: threshold_apply8<5>(s, tie); break;
-          case 6: threshold_apply8<6>(s, tie); break;
-          case 7: threshold_apply8<7>(s, tie); break;
-          default: break;
-        }
-      }
-      exact = __builtin_amdgcn_ballot_w64(tie) != 0ull;   // n >= M keeps every allowed key
+    bool tie = false;
+    if (dense_tile(kt, k0)) {
+      uint32_t win[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) win[qb] = window(kt, k0, qb);
+      threshold_n<true>(s, win, tie);
+    } else {
+      const uint32_t none[QB] = {};
+      threshold_n<false>(s, none, tie);
     }
-    if (exact) rank_apply(kt, j, s, lane);
+    if (__builtin_amdgcn_ballot_w64(tie) != 0ull) rank_apply(kt, j, s, lane);
     if (keep_bits != nullptr) export_bits(kt, k0, s, lane);
   }
 
@@ -504,14 +501,14 @@ struct NmFilter {
     for (int qb = 0; qb < QB; ++qb) {
       const int row = kt.wrow0 + qb * 32 + kt.r32;
       if (row >= kt.Sq) continue;
-      int kbase = k0 + 4 * kt.h;   // key = kbase + c, c a compile-time constant
+      int kbase = k0 + 8 * kt.h;   // key = kbase + elem_key(kb, r), a compile-time offset
       asm volatile("" : "+v"(kbase));
       float* dst = scores + (row_base + row) * kt.Sk + kbase;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+          const int c = elem_key(kb, r);
           if (kbase + c < kt.Sk) dst[c] = s[kb][qb][r];
         }
     }
@@ -533,11 +530,10 @@ struct NmFilter {
       // lanes l and l^32 hold the same row: both stay active through the swap
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        // this lane's 16 bits sit at key offsets (r/4)*8 + 4h + r%4: spread the nibbles 8 apart,
-        // then shift by 4h; merged with lane^32's half
+        // this lane's 16 bits sit at key offsets 16*(r/8) + 8h + r%8: the two bytes 16 apart,
+        // then shifted by 8h; merged with lane^32's half
         const uint32_t x = (kb_bits >> (kb * 16)) & 0xFFFFu;
-        uint32_t word = ((x & 0xFu) | ((x & 0xF0u) << 4) | ((x & 0xF00u) << 8) |
-                         ((x & 0xF000u) << 12)) << (4 * h);
+        uint32_t word = ((x & 0xFFu) | ((x & 0xFF00u) << 8)) << (8 * h);
         word |= __float_as_uint(other_half(__uint_as_float(word), lane));
         if (row < kt.Sq && h == 0 && k0 + kb * 32 < kt.Sk)
           keep_bits[(row_base + row) * W + k0 / 32 + kb] = word;

@@ -72,7 +72,7 @@ struct ExactPolicy {
   __device__ __forceinline__ void mask(int step, f32x16 (&s)[2][QB], int) const {
     const int k0 = first_key(step);
     if (k0 + kKeysPerTile <= Sk) return;
-    const int lim = Sk - k0 - 4 * h;
+    const int lim = Sk - k0 - 8 * h;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -116,10 +116,10 @@ struct SummaryPolicy {
         const int nbits = nKB - 32 * wd;   // >= 1; clears stray padding bits
         bits = keep[wd] & (nbits >= 32 ? 0xFFFFFFFFu : ((1u << nbits) - 1u));
       }
-      const uint32_t lane_bits = bits >> (4 * h);   // element r holds bit (r/4)*8 + r%4 of these
+      const uint32_t lane_bits = bits >> (8 * h);   // element r holds bit (r/8)*16 + r%8 of these
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const uint32_t m = ((lane_bits >> ((r >> 2) * 8 + (r & 3))) & 1u) - 1u;   // ~0: drop
+        const uint32_t m = ((lane_bits >> ((r >> 3) * 16 + (r & 7))) & 1u) - 1u;   // ~0: drop
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[kb][qb][r] = select_neg_inf(s[kb][qb][r], m);
       }

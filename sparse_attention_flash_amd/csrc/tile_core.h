@@ -14,6 +14,12 @@
 // MFMA 32x32x16 bf16 register layout (verified on gfx950 with an in-bounds probe):
 //   A[i][k]: lane i + 32*(k/8), element k%8      B[k][j]: lane j + 32*(k/8), element k%8
 //   C[i][j]: lane j + 32*h holds rows i = (r/4)*8 + 4*h + r%4 in element r (r = 0..15)
+//
+// Key order.  MFMA row i of a 32-key block is fed key kappa(i) = i with bits 2 and 3 exchanged,
+// so element r of lane j + 32*h holds key 16*(r/8) + 8*h + r%8 of the block: every lane holds
+// runs of 8 consecutive keys (two per block), which keeps groups of 4 and of 8 consecutive keys
+// inside one lane.  For P.V the 16-key chunk c of a block is then simply key 16*c + k at the
+// B-operand index k = 8*h + e of element 8*c + e.
 // Transpose read ds_read_b64_tr_b16 (verified likewise): in each group of 16 lanes, source lane j
 // points at 4 consecutive 16-bit elements; output lane i receives element i%4 of source lanes
 // i/4, i/4+4, i/4+8, i/4+12.  Pointing source lane j at V[kb + j/4][db + 4*(j%4)] hands output
@@ -57,6 +63,11 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // head_dim 64 (one layout for K and V): 8 blocks of 8 rows x 8 chunks, row-major, chunk q of row r
 // stored at q ^ f(r) (f a bijection on 8 rows) so 8 consecutive rows at one chunk hit 8 chunks.
 // ------------------------------------------------------------------------------------------------
+// The key fed to MFMA row i of a 32-key block: bits 2 and 3 of i exchanged (see "Key order").
+__device__ __forceinline__ int key_of_row(int i) {
+  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
 template <int D, bool kV>
 struct TileLayout;
 
@@ -75,15 +86,16 @@ struct TileLayout<128, kV> {
   static __device__ __forceinline__ int chunk_off(int r, int q) {
     return (r & 15) * kPitch + ((r >> 4) * 16 + q) * 16;
   }
-  // K rows as MFMA A operands: row 32kb + lane%32, chunk 2ks + lane/32
+  // K rows as MFMA A operands: row 32kb + kappa(lane%32), chunk 2ks + lane/32 (rows 0..15 of a
+  // quarter wave are a permutation of 16 consecutive rows: still one per block)
   static __device__ __forceinline__ int k_off(int lane, int kb, int ks) {
-    return chunk_off((lane & 31) + 32 * kb, 2 * ks + (lane >> 5));
+    return chunk_off(key_of_row(lane & 31) + 32 * kb, 2 * ks + (lane >> 5));
   }
-  // transpose-read source of lane (g = lane/16, j = lane%16): row 32kb + 16c + 4(lane/32) + j/4
-  // + 8hi, columns 32db + 16(g%2) + 4(j%4) .. +3
+  // transpose-read source of lane (g = lane/16, j = lane%16): row 32kb + 16c + 8(lane/32) + j/4
+  // + 4hi, columns 32db + 16(g%2) + 4(j%4) .. +3
   static __device__ __forceinline__ int v_off(int lane, int kb, int c, int hi, int db) {
     const int g = lane >> 4, j = lane & 15, h = lane >> 5;
-    const int r = kb * 32 + c * 16 + 4 * h + (j >> 2) + 8 * hi;
+    const int r = kb * 32 + c * 16 + 8 * h + (j >> 2) + 4 * hi;
     return chunk_off(r, db * 4 + 2 * (g & 1) + ((j & 3) >> 1)) + (j & 1) * 8;
   }
 };
@@ -104,12 +116,12 @@ struct TileLayout<64, kV> {
     return (lane >> 3) * stride_b + swz(lane >> 3, lane & 7) * 16;
   }
   static __device__ __forceinline__ int k_off(int lane, int kb, int ks) {
-    const int row = kb * 32 + (lane & 31);
+    const int row = kb * 32 + key_of_row(lane & 31);
     return row * 128 + swz(row, 2 * ks + (lane >> 5)) * 16;
   }
   static __device__ __forceinline__ int v_off(int lane, int kb, int c, int hi, int db) {
     const int g = lane >> 4, j = lane & 15, h = lane >> 5;
-    return elem(kb * 32 + c * 16 + 4 * h + (j >> 2) + 8 * hi, db * 32 + 16 * (g & 1) + 4 * (j & 3));
+    return elem(kb * 32 + c * 16 + 8 * h + (j >> 2) + 4 * hi, db * 32 + 16 * (g & 1) + 4 * (j & 3));
   }
 };
 
@@ -156,7 +168,7 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 }
 
 // S^T for one 64-key tile: s[kb][qb] is the 32x32 block keys 32*kb.., queries 32*qb..
-// Element r of lane l: key 32*kb + (r/4)*8 + 4*(l/32) + r%4, query 32*qb + l%32.
+// Element r of lane l: key 32*kb + (r/8)*16 + 8*(l/32) + r%8, query 32*qb + l%32.
 // K fragments are read from LDS kPrefetch steps ahead of the MFMAs that use them.
 template <int D, int QB>
 __device__ __forceinline__ void qk_tile(const char* ldsK, const bf16x8 (&qf)[QB][D / 16],
@@ -184,24 +196,27 @@ __device__ __forceinline__ void qk_tile(const char* ldsK, const bf16x8 (&qf)[QB]
   }
 }
 
-// Set element r of s to -inf when off(r) >= lim, off(r) = kb*32 + (r/4)*8 + r%4 being the key's
-// offset inside the tile minus 4*(lane/32).  Pure VGPR arithmetic (shift mask + bitfield select,
+// Set element r of s to -inf when off(r) >= lim, off(r) = kb*32 + (r/8)*16 + r%8 being the key's
+// offset inside the tile minus 8*(lane/32).  Pure VGPR arithmetic (shift mask + bitfield select,
 // one v_bfi_b32): a compare per element would park 64 lane masks in SGPRs.
 __device__ __forceinline__ float select_neg_inf(float x, uint32_t m) {   // m: all ones -> -inf
   return __uint_as_float((0xFF800000u & m) | (__float_as_uint(x) & ~m));
 }
 
+// offset of element r of a lane's s[kb] inside the tile, less 8*(lane/32)
+__device__ __forceinline__ constexpr int elem_key(int kb, int r) {
+  return kb * 32 + (r >> 3) * 16 + (r & 7);
+}
+
 __device__ __forceinline__ void mask_block(f32x16& s, int kb, int lim) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
-    s[r] = select_neg_inf(s[r], (uint32_t)((lim - 1 - off) >> 31));   // all ones when off >= lim
-  }
+  for (int r = 0; r < 16; ++r)
+    s[r] = select_neg_inf(s[r], (uint32_t)((lim - 1 - elem_key(kb, r)) >> 31));   // off >= lim
 }
 
 // Key index (0..63 inside the tile) held in element r of this lane's s[kb][*] block.
 __device__ __forceinline__ int tile_key(int kb, int r, int lane) {
-  return kb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+  return elem_key(kb, r) + (lane >> 5) * 8;
 }
 
 // Value of x held by the lane in the other half of the wavefront (lane ^ 32).

@@ -59,6 +59,12 @@ def test_measured_traffic_only_for_the_profiled_source(tmp_path, monkeypatch):
     assert bench.measured_traffic("good.txt") == 6.0e10
     assert bench.measured_traffic("stale.txt") is None
     assert bench.measured_traffic("missing.txt") is None
+    # each kernel's profile is checked against its own sources
+    nm_good = tmp_path / "nm.txt"
+    nm_good.write_text(f"hbm_bytes_per_launch: 1.0e+9\nsource_digest: "
+                       f"{bench.source_digest(bench.KERNEL_SOURCES['nm'])}\n")
+    assert bench.measured_traffic("nm.txt", "nm") == 1.0e9
+    assert bench.measured_traffic("nm.txt", "skip") is None
 
 
 def test_more_than_one_gpu_is_refused():
@@ -66,3 +72,28 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_wave_flops_count_qk_per_tile_and_pv_per_wave_block():
+    S, D = 256, 64
+    P_tile = bench.tile_pairs(S, S, 128, 64, False)
+    P_wave = bench.tile_pairs(S, S, 32, 64, False)
+    st = np.zeros((1, 1, S // 32, S // 64), np.uint8)
+    st[0, 0, 1, 2] = 1                          # one 32-row block skips one key tile
+    got = bench.wave_skip_flops(st, P_tile, P_wave, D)
+    assert got == 4 * D * S * S - 2 * D * 32 * 64
+    # every block keeps every tile: the dense flops
+    assert bench.wave_skip_flops(np.zeros_like(st), P_tile, P_wave, D) == 4 * D * S * S
+
+
+def test_roofline_block_fields():
+    r = bench.roofline("mfma", 1250.0)
+    assert r["frac"] == 0.5 and r["peak"] == 2500.0 and r["unit"] == "TFLOP/s"
+    h = bench.roofline("hbm", 4000.0)
+    assert h["frac"] == 0.5 and h["unit"] == "GB/s" and h["traffic"] is None
+
+
+def test_unknown_leg_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--only", "nope"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0 and "unknown leg" in r.stderr

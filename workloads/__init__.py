@@ -7,7 +7,7 @@ imported here.  Every generator is a function of (seed, shape) alone and returns
 
 Generators (each a stand-in for a workload the pages describe but do not ship):
 
-* ``gen_iid``   -- Q, K, V iid N(0, 1).
+* ``gen_iid``   -- Q, K, V iid N(0, 1) (``gen_iid_f32``: the same values before bf16 rounding).
 * ``gen_llm``   -- LLM-prefill-like: per (batch, KV head) an AR(1) latent (rho 0.9, stationary
   N(0, I)) shared by Q and K, so nearby tokens attend to each other; a per-KV-head unit direction u
   with amplitude alpha = sqrt(sink_nats * sqrt(D)) added to every query and to the first
@@ -76,6 +76,20 @@ def gen_iid(seed, B, Sq, Sk, Hq, Hkv, D):
         for h in range(Hkv):
             k[b, :, h] = to_bf16_bits(_normal(_rng(seed, 2, b, h), (Sk, D)))
             v[b, :, h] = to_bf16_bits(_normal(_rng(seed, 3, b, h), (Sk, D)))
+    return q, k, v
+
+
+def gen_iid_f32(seed, B, Sq, Sk, Hq, Hkv, D):
+    """The float32 values gen_iid draws, before their rounding to bf16 (same streams)."""
+    q = np.empty((B, Sq, Hq, D), np.float32)
+    k = np.empty((B, Sk, Hkv, D), np.float32)
+    v = np.empty((B, Sk, Hkv, D), np.float32)
+    for b in range(B):
+        for h in range(Hq):
+            q[b, :, h] = _normal(_rng(seed, 1, b, h), (Sq, D))
+        for h in range(Hkv):
+            k[b, :, h] = _normal(_rng(seed, 2, b, h), (Sk, D))
+            v[b, :, h] = _normal(_rng(seed, 3, b, h), (Sk, D))
     return q, k, v
 
 
