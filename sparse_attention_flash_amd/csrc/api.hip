@@ -91,7 +91,7 @@ sa_status from_hip(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; 
 
 // Decode: split plan and workspace layout, the same for the size query and the call.
 struct DecodePlan {
-  int GM, nKT, nsplit, tps;
+  int GM, nKT, nsplit, tps, fused;
   size_t off_scores, off_tmax, off_pm, off_pl, off_po, bytes;
 };
 
@@ -106,6 +106,22 @@ sa_status plan_decode(const sa_attn_desc* d, float lambda, int32_t num_splits, D
   p->GM = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
   p->nKT = (int)(((int64_t)d->seqlen_k + d->block_k - 1) / d->block_k);
   const int64_t units = (int64_t)d->batch * d->heads_kv;
+  // One workgroup per (batch, KV head) holding its heads' scores for the whole cache in LDS, when
+  // they fit: no workspace and no exchange between workgroups.  Chosen whenever the call runs one
+  // split -- asked for, or lambda > 1, whose decisions depend on the order of the kept tiles.
+  // With several splits the key axis spreads over more workgroups than there are (batch, KV head)
+  // units, which streams faster when those units are fewer than the CUs (measured on the
+  // 16 x 8-KV-head decode workload: 119 us per step with two splits against 136 us whole-sequence).
+  const bool fits = p->GM <= sa::kFusedMaxGM &&
+                    (int64_t)p->GM * p->nKT * d->block_k * 4 <= sa::kFusedScoreBytes;
+  p->fused = fits && (num_splits == 1 || (num_splits == 0 && lambda > 1.f));
+  if (p->fused) {
+    p->nsplit = 1;
+    p->tps = p->nKT;
+    p->off_scores = p->off_tmax = p->off_pm = p->off_pl = p->off_po = 0;
+    p->bytes = 256;   // no workspace is used; the callers' contract keeps a non-empty buffer
+    return SA_OK;
+  }
   int ns;
   if (lambda > 1.f) {
     // decisions depend on the order of the kept tiles: one split walks them all
@@ -160,6 +176,8 @@ sa_status decode_run(const sa_attn_desc& d, const DecodePlan& p, const void* q, 
   a.nKT = p.nKT;
   a.nsplit = p.nsplit;
   a.tiles_per_split = p.tps;
+  a.fused = p.fused;
+  a.dbg_tmax = dbg_tile_rowmax;
   a.scores = reinterpret_cast<float*>(ws + p.off_scores);
   a.tmax = dbg_tile_rowmax != nullptr ? dbg_tile_rowmax : reinterpret_cast<float*>(ws + p.off_tmax);
   a.part_m = reinterpret_cast<float*>(ws + p.off_pm);

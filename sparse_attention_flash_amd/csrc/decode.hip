@@ -537,8 +537,335 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeArgs a) {
     a.lse[bh] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
+// ---- whole-sequence decode: one workgroup per (batch, KV head) -------------------------------------
+// When one workgroup owns every key of its (batch, KV head), the decisions need no exchange between
+// workgroups and the scores of the G heads can stay in LDS from the K pass to the V pass:
+//   1 scores: the waves stride over 64-key chunks (K rows straight into MFMA operands, the next
+//     chunk loaded while the current one is multiplied) and write S and each chunk's max per head
+//     into LDS;
+//   2 decisions: one wave per head walks the tiles in order -- a wave-wide prefix-max scan 64 tiles
+//     at a time for lambda <= 1 (a skipped tile cannot raise the running max), the running max for
+//     lambda > 1 -- writing the keep bits, tile states, counters and the head's exponent reference
+//     r (the max of its kept tile maxima, so that P = 2^(t - r) <= 1 needs no rescaling);
+//   3 P.V: the waves stride over the chunks of tiles some head keeps (the V rows of the next chunk
+//     loaded while the current one is reduced), with P from the LDS scores; the waves' partial sums
+//     are then added in LDS (reusing the score buffer) and O and the natural-log LSE written.
+// K and V are each read once; nothing goes through device memory between the passes.
+constexpr int kFusedWaves = 8;
+constexpr int kFusedThreads = 64 * kFusedWaves;
+
+template <int D, int GM>
+__global__ __launch_bounds__(kFusedThreads) void decode_fused(DecodeArgs a) {
+  constexpr int KS = D / 16;
+  constexpr int LPK = D / 8;          // lanes per V row (16 bytes each)
+  constexpr int KPI = 64 / LPK;       // V rows per wave-wide load
+  constexpr int kIt = 64 / KPI;
+  constexpr int GQ = (GM + 3) / 4;    // 16-byte groups of P per key
+  constexpr int kMaxChunks = kFusedScoreBytes / (4 * 64);   // GM * chunks <= this (host check)
+  const AttnGeom& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, hl = lane >> 5;
+  const int G = g.Hq / g.Hkv;
+  const int BC = a.block_k, cpt = BC / 64;
+  const int hk = (int)(blockIdx.x % g.Hkv), b = (int)(blockIdx.x / g.Hkv);
+  int len = g.Sk;
+  if (a.seqlens_k != nullptr) len = min(max(a.seqlens_k[b], 0), g.Sk);
+  const int nKT = a.nKT;
+  const int nvis = (len + BC - 1) / BC;   // tiles holding a key of the sequence
+  const int nch = nvis * cpt;             // their 64-key chunks
+  const int row_len = nKT * BC;           // LDS score row stride (keys)
+  const int cstride = nKT * cpt;          // chunk-maxima row stride
+
+  __shared__ __attribute__((aligned(16))) float sc[kFusedScoreBytes / 4];   // [GM][row_len]
+  __shared__ float cmax[kMaxChunks];        // [G][cstride] chunk maxima, log2 domain
+  __shared__ uint32_t kbits[kMaxChunks];    // per tile: bit h set when head h keeps it
+  __shared__ uint16_t klist[kMaxChunks];    // tiles kept by some head, ascending
+  __shared__ int nkept_s;
+  __shared__ float ref_s[GM];
+  __shared__ __attribute__((aligned(16))) float pbuf[kFusedWaves][64][4 * GQ];
+  __shared__ float lred[kFusedWaves][GM];
+
+  for (int t = tid; t < nKT; t += kFusedThreads) kbits[t] = 0u;
+
+  // ---- 1: scores into LDS ----
+  bf16x8 qf[KS];
+  {
+    const __bf16* qp = (const __bf16*)g.q + b * g.qs[0] + (hk * G + min(col, G - 1)) * g.qs[2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 x = *(const bf16x8*)(qp + 16 * ks + 8 * hl);
+      if (col >= G) x = bf16x8{};
+      qf[ks] = x;
+    }
+  }
+  {
+    const __bf16* kslab = (const __bf16*)g.k + b * g.ks[0] + hk * g.ks[2];
+    const auto krs = slab_rsrc(kslab, g.ks[1], len, D);
+    const int kstride_b = (int)(g.ks[1] * 2);
+    // this wave's chunks c = wave + kFusedWaves * i; the prefetch index is clamped (unconditional
+    // loads keep the compiler's waits from draining them)
+    const int nq = nch > wave ? (nch - wave + kFusedWaves - 1) / kFusedWaves : 0;
+    auto key_of = [&](int i) { return (wave + kFusedWaves * i) * 64; };
+    auto load_chunk = [&](bf16x8 (&kv)[2][KS], int i) {
+      const int key0 = key_of(i);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int off = (key0 + 32 * kb + col) * kstride_b + 16 * hl;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kv[kb][ks] = __builtin_bit_cast(bf16x8, load16(krs, off + 32 * ks));
+      }
+    };
+    auto consume = [&](const bf16x8 (&kv)[2][KS], int i) {
+      const int key0 = key_of(i);
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(kv[kb][ks], qf[ks], s[kb]);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        mask_rows(s[kb], kb, len - key0 - 4 * hl);   // keys past the sequence: -inf
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        if (col < G) {
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4)
+            *(f32x4*)&sc[col * row_len + key0 + 32 * kb + 8 * i4 + 4 * hl] =
+                f32x4{s[kb][4 * i4], s[kb][4 * i4 + 1], s[kb][4 * i4 + 2], s[kb][4 * i4 + 3]};
+        }
+      }
+      const float m = half_max(mx);
+      if (hl == 0 && col < G) cmax[col * cstride + key0 / 64] = m * g.c32;
+    };
+    bf16x8 kva[2][KS], kvb[2][KS];
+    if (nq > 0) {
+      load_chunk(kva, 0);
+      for (int i = 0; i < nq; i += 2) {
+        load_chunk(kvb, min(i + 1, nq - 1));
+        consume(kva, i);
+        load_chunk(kva, min(i + 2, nq - 1));
+        if (i + 1 < nq) consume(kvb, i + 1);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 2: decisions, one wave per head ----
+  for (int h = wave; h < G; h += kFusedWaves) {
+    const int64_t unit = (int64_t)b * g.Hq + hk * G + h;
+    auto tile_max = [&](int t) {   // t < nvis
+      float m = cmax[h * cstride + t * cpt];
+      if (cpt == 2) m = fmaxf(m, cmax[h * cstride + t * cpt + 1]);
+      return m;
+    };
+    float ref = -INFINITY;
+    unsigned vis_n = 0u, skip_n = 0u;
+    if (a.L32 <= 0.f) {
+      float carry = -INFINITY;
+      for (int j0 = 0; j0 < nKT; j0 += 64) {
+        const int j = j0 + lane;
+        const bool in = j < nKT, vis = j < nvis;
+        const float M = vis ? tile_max(j) : -INFINITY;
+        float incl = M;   // inclusive prefix max over the lanes
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const float up = __shfl_up(incl, d, 64);
+          if (lane >= d) incl = fmaxf(incl, up);
+        }
+        float excl = __shfl_up(incl, 1, 64);
+        excl = lane == 0 ? carry : fmaxf(carry, excl);
+        const bool keep = vis && !(M < excl + a.L32);
+        if (keep) atomicOr(&kbits[j], 1u << h);
+        ref = fmaxf(ref, keep ? M : -INFINITY);
+        vis_n += __popcll(__ballot(vis));
+        skip_n += __popcll(__ballot(vis && !keep));
+        if (in && a.tile_state != nullptr) a.tile_state[unit * nKT + j] = vis ? (keep ? 0 : 1) : 2;
+        if (in && a.dbg_tmax != nullptr) a.dbg_tmax[unit * nKT + j] = M;
+        carry = fmaxf(carry, __shfl(incl, 63, 64));
+      }
+      for (int d = 1; d < 64; d <<= 1) ref = fmaxf(ref, __shfl_xor(ref, d, 64));
+    } else {
+      // the running max of the kept tiles, in order (every lane walks the same sequence)
+      float m = -INFINITY;
+      for (int j0 = 0; j0 < nKT; j0 += 64) {
+        const int jl = j0 + lane;
+        const float Ml = jl < nvis ? tile_max(jl) : -INFINITY;
+        if (jl < nKT && a.dbg_tmax != nullptr) a.dbg_tmax[unit * nKT + jl] = Ml;
+        const int n = min(64, nKT - j0);
+        for (int jj = 0; jj < n; ++jj) {
+          const int jt = j0 + jj;
+          const float M = __shfl(Ml, jj, 64);
+          const bool vis = jt < nvis;
+          const bool keep = vis && !(M < m + a.L32);
+          if (keep) {
+            m = fmaxf(m, M);
+            ref = fmaxf(ref, M);
+          }
+          vis_n += vis ? 1u : 0u;
+          skip_n += (vis && !keep) ? 1u : 0u;
+          if (lane == 0) {
+            if (keep) atomicOr(&kbits[jt], 1u << h);
+            if (a.tile_state != nullptr) a.tile_state[unit * nKT + jt] = vis ? (keep ? 0 : 1) : 2;
+          }
+        }
+      }
+    }
+    if (lane == 0) {
+      ref_s[h] = ref;
+      if (a.counters != nullptr) {
+        atomicAdd(&a.counters[2 * unit], vis_n);
+        atomicAdd(&a.counters[2 * unit + 1], skip_n);
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {   // the tiles kept by some head, in order
+    int n = 0;
+    for (int t0 = 0; t0 < nvis; t0 += 64) {
+      const int t = t0 + lane;
+      const bool kept = t < nvis && kbits[t] != 0u;
+      const uint64_t m = __ballot(kept);
+      if (kept) klist[n + __popcll(m & ((1ull << lane) - 1ull))] = (uint16_t)t;
+      n += __popcll(m);
+    }
+    if (lane == 0) nkept_s = n;
+  }
+  __syncthreads();
+
+  // ---- 3: P.V over the kept chunks ----
+  const int sub = lane / LPK, c = lane % LPK;
+  float ref[GM];
+#pragma unroll
+  for (int h = 0; h < GM; ++h) ref[h] = h < G ? ref_s[h] : -INFINITY;
+  float acc[GM][8];
+  float ls[GM];
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    ls[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+  {
+    const __bf16* vslab = (const __bf16*)g.v + b * g.vs[0] + hk * g.vs[2];
+    const auto vrs = slab_rsrc(vslab, g.vs[1], len, D);
+    const int vstride_b = (int)(g.vs[1] * 2);
+    float (*pw)[4 * GQ] = pbuf[wave];
+    const int nq_all = nkept_s * cpt;
+    const int nq = nq_all > wave ? (nq_all - wave + kFusedWaves - 1) / kFusedWaves : 0;
+    auto chunk_of = [&](int i) { return wave + kFusedWaves * i; };   // index into the kept chunks
+    auto key_of = [&](int i) {
+      const int q = chunk_of(i);
+      return (int)klist[q / cpt] * BC + (q % cpt) * 64;
+    };
+    auto load_chunk = [&](u32x4 (&vv)[kIt], int i) {
+      const int key0 = key_of(i);
+#pragma unroll
+      for (int it = 0; it < kIt; ++it)
+        vv[it] = load16(vrs, (key0 + sub + it * KPI) * vstride_b + c * 16);
+    };
+    auto reduce_chunk = [&](const u32x4 (&vv)[kIt], int i) {
+      const int q = chunk_of(i);
+      const int key0 = key_of(i);
+      const uint32_t kb = kbits[klist[q / cpt]];
+      // P of the 64 keys, one key per lane, into this wave's LDS slot; l from the same values
+      const bool valid = key0 + lane < len;
+#pragma unroll
+      for (int h = 0; h < 4 * GQ; ++h) {
+        float p = 0.f;
+        if (h < G && ((kb >> h) & 1u) && valid)
+          p = __builtin_amdgcn_exp2f(sc[(h < GM ? h : 0) * row_len + key0 + lane] * g.c32 -
+                                     ref[h < GM ? h : 0]);
+        if (h < GM) ls[h < GM ? h : 0] += p;
+        pw[lane][h] = p;
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): P is in LDS for the whole wave
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int it = 0; it < kIt; ++it) {
+        const int kl = sub + it * KPI;   // key within the 64
+        float vf[8];
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const uint32_t w = vv[it][i4];
+          vf[2 * i4] = bf16_lo(w);
+          vf[2 * i4 + 1] = bf16_hi(w);
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < GQ; ++q4) {
+          const f32x4 p4 = *(const f32x4*)&pw[kl][4 * q4];
+#pragma unroll
+          for (int hh = 0; hh < 4; ++hh) {
+            const int h = 4 * q4 + hh;
+            if (h >= GM) break;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] += p4[hh] * vf[e];
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();   // every lane has read P before the next chunk rewrites it
+    };
+    if (nq > 0) {
+      u32x4 vva[kIt], vvb[kIt];
+      load_chunk(vva, 0);
+      for (int i = 0; i < nq; i += 2) {
+        load_chunk(vvb, min(i + 1, nq - 1));
+        reduce_chunk(vva, i);
+        load_chunk(vva, min(i + 2, nq - 1));
+        if (i + 1 < nq) reduce_chunk(vvb, i + 1);
+      }
+    }
+  }
+
+  // sum over the key slots of each wave, then over the waves (the score buffer is free now)
+  __syncthreads();
+  float* red = sc;   // [kFusedWaves][GM][D]
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    for (int d = LPK; d < 64; d <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], d, 64);
+    }
+    float l = ls[h];
+    for (int d = 1; d < 64; d <<= 1) l += __shfl_xor(l, d, 64);
+    if (sub == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[(wave * GM + h) * D + 8 * c + e] = acc[h][e];
+    }
+    if (lane == 0) lred[wave][h] = l;
+  }
+  __syncthreads();
+  for (int i = tid; i < G * D; i += kFusedThreads) {
+    const int h = i / D, d = i % D;
+    float o = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kFusedWaves; ++w) {
+      o += red[(w * GM + h) * D + d];
+      l += lred[w][h];
+    }
+    const int hq = hk * G + h;
+    __bf16* op = (__bf16*)g.o + b * g.os[0] + hq * g.os[2];
+    op[d] = (__bf16)(l > 0.f ? o / l : 0.f);
+    if (d == 0 && a.lse != nullptr)
+      a.lse[(int64_t)b * g.Hq + hq] = l > 0.f ? (ref_s[h] + __log2f(l)) * 0.69314718055994531f
+                                              : -INFINITY;
+  }
+}
+
+template <int D, int GM>
+hipError_t launch_fused(const DecodeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_fused<D, GM>), dim3(a.g.B * a.g.Hkv), dim3(kFusedThreads), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
 template <int D, int GM>
 hipError_t launch_dg(const DecodeArgs& a, hipStream_t stream) {
+  if constexpr (GM <= kFusedMaxGM) {
+    if (a.fused) return launch_fused<D, GM>(a, stream);
+  }
   const int units = a.g.B * a.g.Hkv * a.nsplit;
   hipLaunchKernelGGL((decode_scores<D, GM>), dim3(units), dim3(kDecThreads), 0, stream, a);
   hipError_t e = hipGetLastError();

@@ -52,12 +52,19 @@ struct SkipNmArgs {
 // Decode-phase skip-softmax (one query token per head, key axis split over workgroups).
 constexpr int kMaxTilesPerSplit = 4096;
 
+// Whole-sequence decode: one workgroup per (batch, KV head) keeps the scores of its G heads over
+// the whole key range in LDS, when they fit in this many bytes (GM <= kFusedMaxGM).
+constexpr int kFusedScoreBytes = 128 * 1024;
+constexpr int kFusedMaxGM = 8;
+
 struct DecodeArgs {
   AttnGeom g;                           // Sq == 1, non-causal
   float L32;
   const int32_t* seqlens_k;             // optional [B], keys per sequence (clamped to [0, Sk])
   int block_k;                          // 64 or 128: the decision tile
   int nKT, nsplit, tiles_per_split;
+  int fused;                            // 1: one whole-sequence kernel (nsplit == 1, no workspace)
+  float* dbg_tmax;                      // optional [B, Hq, nKT] export of the tile maxima (fused)
   float* scores;                        // workspace [B, Hkv, GM, nKT*block_k] raw q.k (GM >= G)
   float* tmax;                          // [B, Hq, nKT] tile maxima, log2 domain
   float* part_m;                        // [B, Hq, nsplit] split reference (max of kept maxima)

@@ -83,13 +83,17 @@ def check(q, k, v, lens, lam, BC, tag, num_splits=0):
     return g
 
 
+# num_splits 1 takes the whole-sequence kernel (one workgroup per batch and KV head, scores in
+# LDS) wherever its scores fit; 0 lets the library choose: the key-axis split (three kernels) for
+# lambda <= 1, the whole-sequence kernel for lambda > 1.
+@pytest.mark.parametrize("splits", [0, 1])
 @pytest.mark.parametrize("lam", [0.0, 0.3, 1.0, 3.0])
 @pytest.mark.parametrize("BC", [64, 128])
-def test_llm_decode_ragged(lam, BC):
+def test_llm_decode_ragged(lam, BC, splits):
     q, k, v, lens = W.gen_llm_decode(31, 4, 1500, 8, 2, 128)
     lens[1] = 1          # a one-key sequence
     lens[2] = 700        # a ragged last tile
-    g = check(q, k, v, lens, lam, BC, "llm gqa 8/2 cap 1500")
+    g = check(q, k, v, lens, lam, BC, "llm gqa 8/2 cap 1500", num_splits=splits)
     if lam >= 1.0:
         assert (g["st"] == 1).sum() > 0
 
@@ -103,18 +107,32 @@ def test_split_count_does_not_change_decisions(splits):
     assert np.array_equal(g["rm"], ref["rm"])
 
 
+@pytest.mark.parametrize("splits", [0, 1])
 @pytest.mark.parametrize("Hq,Hkv,D", [(4, 4, 128), (16, 2, 128), (32, 2, 128), (8, 1, 64),
                                       (6, 2, 64), (5, 1, 128)])
-def test_head_groups_and_head_dims(Hq, Hkv, D):
+def test_head_groups_and_head_dims(Hq, Hkv, D, splits):
     q, k, v, lens = W.gen_llm_decode(33, 2, 900, Hq, Hkv, D)
-    check(q, k, v, lens, 0.8, 64, f"G={Hq // Hkv} D={D}")
+    check(q, k, v, lens, 0.8, 64, f"G={Hq // Hkv} D={D}", num_splits=splits)
 
 
-def test_empty_sequence_and_no_lengths():
+@pytest.mark.parametrize("splits", [0, 1])
+def test_empty_sequence_and_no_lengths(splits):
     q, k, v, lens = W.gen_llm_decode(34, 3, 300, 4, 2, 128)
     lens[0] = 0
-    check(q, k, v, lens, 0.5, 64, "empty sequence")
-    check(q, k, v, None, 0.5, 64, "no seqlens")
+    check(q, k, v, lens, 0.5, 64, "empty sequence", num_splits=splits)
+    check(q, k, v, None, 0.5, 64, "no seqlens", num_splits=splits)
+
+
+def test_whole_sequence_kernel_at_its_size_limit():
+    """The largest cache whose scores still fit in LDS (G 4, 8192 keys; G 1, 32768 keys at 128-key
+    tiles), one split: the whole-sequence kernel; the split path on the same inputs decides
+    identically."""
+    for Hq, Hkv, S, BC in ((8, 2, 8192, 64), (2, 2, 32768, 128)):
+        q, k, v, lens = W.gen_llm_decode(35, 2, S, Hq, Hkv, 128)
+        g = check(q, k, v, lens, 0.7, BC, f"limit G={Hq // Hkv} S={S}", num_splits=1)
+        ref = run_gpu(q, k, v, lens, 0.7, BC, num_splits=4)
+        assert np.array_equal(g["st"], ref["st"])
+        assert np.array_equal(g["rm"], ref["rm"])
 
 
 def test_full_size_decode_workload():
