@@ -14,8 +14,8 @@
 // starts from the max of the earlier splits' tile maxima.  (lambda > 1 runs as one split.)
 //
 // Decode reads every K row once and each kept V row once for G query heads: about 4 flops per
-// byte, so the kernels are bound by the K/V stream.  K and V are read straight into registers
-// with 16-byte loads, and each 64-key chunk's loads are in flight while the previous chunk is used:
+// byte, so the kernels are bound by the K/V stream.  Each 64-key chunk's loads are in flight while
+// the previous chunk is used:
 //   1 decode_scores   q.k for the G heads of a KV head on MFMA (the heads as the columns of
 //                     S^T = K.Q^T), written to a small fp32 workspace, and each tile's maximum;
 //   2 decode_attend   per split: the decisions (for lambda <= 1 a wave-wide prefix-max scan over
@@ -28,7 +28,7 @@
 #include <mutex>
 
 #include "kernels.h"
-#include "tile_core.h"
+#include "mainloop.h"
 
 // The allocation-free decode entry point keeps its workspace here (scores, tile maxima, split
 // partials).  Host code never uses this name as an address: it is a host-side stand-in for the
@@ -106,38 +106,47 @@ __device__ __forceinline__ void mask_rows(f32x16& s, int kb, int lim) {
 }
 
 // ---- 1: scores and tile maxima --------------------------------------------------------------------
-// S^T = K.Q^T on v_mfma_f32_32x32x16_bf16, one 32-key block at a time: A = 32 K rows (lane l: key
-// l%32, the 8 values at d = 16ks + 8(l/32)), B = Q^T with the G heads as columns (columns past G
+// S^T = K.Q^T on v_mfma_f32_32x32x16_bf16 with the G heads as the columns of Q^T (columns past G
 // are zero).  Only G of the 32 columns do useful work, but the matrix cores still need about an
 // eighth of the issue cycles of the same dot products on the VALU, so the kernel stays bound by
-// the K stream.  Lane l then holds, for head l%32, keys 8i + 4(l/32) + {0..3} in elements
-// 4i..4i+3.  Scores go to the workspace head-major, [GM][nKT*block_k] per (batch, KV head).
-template <int D, int GM>
+// the K stream.
+//
+// Each wave streams its own 64-key chunks (tiles t0 + wave + kDecWaves*i) HBM -> LDS with the
+// direct-to-LDS copies of the prefill kernels, 16 lanes on each 256-byte row, one chunk in flight
+// while the previous one is multiplied, and reads the MFMA operands from LDS.  Loading K straight
+// into operand registers instead makes every instruction touch 32 rows at 32 bytes each, so each
+// 128-byte line is fetched by four instructions and, with two chunks in flight per wave, can fall
+// out of the 32 KB L1 between them (measured on 16 x 8 KV heads x 8192 keys: 63.4 us per pass that
+// way, 56.5 us through LDS).  Scores go to the workspace head-major and in key order,
+// [GM][nKT*block_k] per (batch, KV head).
+template <int D, int GM, int CPT>
 __global__ __launch_bounds__(kDecThreads) void decode_scores(DecodeArgs a) {
   constexpr int KS = D / 16;   // MFMA k-steps per key block
+  using L = KLayout<D>;
+  using DmaK = Dma<L, 1>;      // one wave copies a whole chunk
   const AttnGeom& g = a.g;
   const DecUnit u = dec_unit(a);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, hl = lane >> 5;
   const int G = g.Hq / g.Hkv;
-  const int BC = a.block_k;
+  constexpr int BC = 64 * CPT;
   const int64_t row_len = (int64_t)a.nKT * BC;   // scores row stride (a multiple of 64 keys)
 
-  bf16x8 qf[KS];
+  bf16x8 qf[1][KS];
   {
     const __bf16* qp = (const __bf16*)g.q + u.b * g.qs[0] + (u.hk * G + min(col, G - 1)) * g.qs[2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8 x = *(const bf16x8*)(qp + 16 * ks + 8 * hl);
       if (col >= G) x = bf16x8{};
-      qf[ks] = x;
+      qf[0][ks] = x;
     }
   }
   const __bf16* kslab = (const __bf16*)g.k + u.b * g.ks[0] + u.hk * g.ks[2];
-  const auto krs = slab_rsrc(kslab, g.ks[1], u.len, D);
   const int kstride_b = (int)(g.ks[1] * 2);
   float* sc = a.scores + ((int64_t)u.b * g.Hkv + u.hk) * GM * row_len;
+  __shared__ __attribute__((aligned(1024))) char kbuf[kDecWaves][2][L::kBytes];
   // A chunk's scores go through LDS so that the whole wave stores them with full 16-byte lanes
   // (the lanes holding them are only 2*GM of 64).
   __shared__ __attribute__((aligned(16))) float sbuf[kDecWaves][GM][64];
@@ -149,48 +158,27 @@ __global__ __launch_bounds__(kDecThreads) void decode_scores(DecodeArgs a) {
       a.tmax[((int64_t)u.b * g.Hq + u.hk * G + lane) * a.nKT + t] = -INFINITY;
   }
 
-  // This wave's visited tiles t = t0 + wave + 4i as a stream of 64-key chunks; chunk q+1 is loaded
-  // while chunk q is multiplied (two register buffers).  The prefetches are unconditional (the
-  // index is clamped, so the tail re-reads the last chunk): a prefetch under a branch would make
-  // every later use wait for all loads in flight.
   const int t_end = min(u.t1, u.nvis);
   const int ntile = t_end > u.t0 + wave ? (t_end - (u.t0 + wave) + kDecWaves - 1) / kDecWaves : 0;
-  const int cpt = BC / 64;   // chunks per tile
+  constexpr int cpt = CPT;   // chunks per tile
   const int nq = ntile * cpt;
   auto chunk_key0 = [&](int q) { return (u.t0 + wave + kDecWaves * (q / cpt)) * BC + (q % cpt) * 64; };
-  auto load_chunk = [&](bf16x8 (&kv)[2][KS], int q) {
+  const auto lo = DmaK::lane_offsets(kstride_b, 0, lane);
+  // Chunk q into LDS buffer q%2: rows past the sequence are outside the copy's byte range and
+  // arrive as zeros (the range covers at most the chunk's 64 rows).
+  auto issue = [&](int q) {
     const int key0 = chunk_key0(q);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int off = (key0 + 32 * kb + col) * kstride_b + 16 * hl;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kv[kb][ks] = __builtin_bit_cast(bf16x8, load16(krs, off + 32 * ks));
-    }
+    const int rows = min(u.len - key0, 64);
+    const int bytes = rows > 0 ? (rows - 1) * kstride_b + D * 2 : 0;
+    DmaK::copy(kbuf[wave][q & 1], kslab + (int64_t)key0 * g.ks[1], bytes, kstride_b, lo, 0);
   };
-  float mx = -INFINITY;   // running max of this lane's keys in the current tile (its head)
-  auto consume = [&](const bf16x8 (&kv)[2][KS], int q) {
+  float mx = -INFINITY;     // running max of this lane's keys in the current tile (its head)
+  float tile_m = -INFINITY; // the last finished tile's max of head col, in the log2 domain
+  // The global stores of chunk q: its scores from the LDS staging buffer and, when it ends a tile,
+  // the tile's max.  They are issued one iteration late, just before the next copy, so that the
+  // wait for that copy never waits on stores younger than it.
+  auto flush = [&](int q) {
     const int key0 = chunk_key0(q);
-    f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(kv[kb][ks], qf[ks], s[kb]);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // keys past the sequence: -inf (their rows read as zeros)
-      mask_rows(s[kb], kb, u.len - key0 - 4 * hl);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      if (col < GM) {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-          *(f32x4*)&sw[col][32 * kb + 8 * i4 + 4 * hl] =
-              f32x4{s[kb][4 * i4], s[kb][4 * i4 + 1], s[kb][4 * i4 + 2], s[kb][4 * i4 + 3]};
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the chunk's scores are in LDS
-    __builtin_amdgcn_wave_barrier();
     // GM rows of 64 keys = GM*16 lanes of 16 bytes
 #pragma unroll
     for (int r = 0; r < (GM * 16 + 63) / 64; ++r) {
@@ -200,26 +188,48 @@ __global__ __launch_bounds__(kDecThreads) void decode_scores(DecodeArgs a) {
         *(f32x4*)(sc + hh * row_len + key0 + k4) = *(const f32x4*)&sw[hh][k4];
       }
     }
-    __builtin_amdgcn_wave_barrier();   // read before the next chunk rewrites the buffer
-    if (q % cpt == cpt - 1) {
-      // tile max of head col over both lane halves, in the log2 domain
+    if (q % cpt == cpt - 1 && hl == 0 && col < G) {
       const int t = u.t0 + wave + kDecWaves * (q / cpt);
-      const float m = half_max(mx);
-      if (hl == 0 && col < G)
-        a.tmax[((int64_t)u.b * g.Hq + u.hk * G + col) * a.nKT + t] = m * g.c32;
-      mx = -INFINITY;
+      a.tmax[((int64_t)u.b * g.Hq + u.hk * G + col) * a.nKT + t] = tile_m;
     }
   };
-  bf16x8 kva[2][KS], kvb[2][KS];
-  if (nq > 0) {
-    load_chunk(kva, 0);
-    for (int q = 0; q < nq; q += 2) {
-      load_chunk(kvb, min(q + 1, nq - 1));
-      consume(kva, q);
-      load_chunk(kva, min(q + 2, nq - 1));
-      if (q + 1 < nq) consume(kvb, q + 1);
+  if (nq > 0) issue(0);
+  for (int q = 0; q < nq; ++q) {
+    // chunk q is in LDS (the stores of chunk q-2, issued before it, are done too)
+    wait_vmcnt<0>();
+    if (q > 0) {
+      flush(q - 1);
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the staging buffer is read
+      __builtin_amdgcn_wave_barrier();
     }
+    // chunk q+1 into the other buffer, whose operands the MFMAs of chunk q-1 read
+    if (q + 1 < nq) issue(q + 1);
+    const int key0 = chunk_key0(q);
+    f32x16 s[2][1];
+    qk_tile<D, 1>(kbuf[wave][q & 1], qf, s, lane);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      // keys past the sequence (only in its last chunk): -inf
+      if (key0 + 64 > u.len) mask_block(s[kb][0], kb, u.len - key0 - 8 * hl);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][0][i]);
+      // element r holds key 32kb + 16(r/8) + 8hl + r%8: two runs of 8 consecutive keys
+      if (col < GM) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          *(f32x4*)&sw[col][32 * kb + 16 * (i4 >> 1) + 8 * hl + 4 * (i4 & 1)] =
+              f32x4{s[kb][0][4 * i4], s[kb][0][4 * i4 + 1], s[kb][0][4 * i4 + 2],
+                    s[kb][0][4 * i4 + 3]};
+      }
+    }
+    if (q % cpt == cpt - 1) {
+      tile_m = half_max(mx) * g.c32;   // tile max of head col over both lane halves
+      mx = -INFINITY;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the chunk's scores are in LDS
+    __builtin_amdgcn_wave_barrier();
   }
+  if (nq > 0) flush(nq - 1);
 }
 
 // ---- 2: decisions and P.V over kept tiles ---------------------------------------------------------
@@ -341,7 +351,7 @@ __device__ __forceinline__ void decide_tiles(const DecodeArgs& a, const DecUnit&
   }
 }
 
-template <int D, int GM>
+template <int D, int GM, int CPT>
 __global__ __launch_bounds__(kDecThreads) void decode_attend(DecodeArgs a) {
   constexpr int LPK = D / 8;
   constexpr int KPI = 64 / LPK;
@@ -353,7 +363,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attend(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int sub = lane / LPK, c = lane % LPK;
   const int G = g.Hq / g.Hkv;
-  const int BC = a.block_k;
+  constexpr int BC = 64 * CPT;
 
   __shared__ float pre[kDecWaves][GM];
   __shared__ float ref_s[GM];
@@ -395,9 +405,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_attend(DecodeArgs a) {
   const float* sc = a.scores + ((int64_t)u.b * g.Hkv + u.hk) * GM * row_len;
   float (*pw)[4 * GQ] = pbuf[wave];
 
-  // This wave's kept tiles t = t0 + wave + 4i (kept by some head) listed in LDS, then walked as
-  // 64-key chunks; the V rows and scores of chunk q+1 are loaded while chunk q is reduced.  The
-  // prefetches are unconditional (clamped index), so the compiler's waits leave them in flight.
+  // This wave's kept tiles t = t0 + wave + kDecWaves*i (kept by some head) listed in LDS, then
+  // walked as 64-key chunks; the V rows and scores of chunk q+1 are loaded while chunk q is
+  // reduced.  The prefetches are unconditional (clamped index), so the compiler's waits leave them
+  // in flight.
   uint16_t* list = klist[wave];
   int nkept = 0;
   for (int i0 = 0; u.t0 + wave + kDecWaves * i0 < u.t1; i0 += 64) {
@@ -409,7 +420,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attend(DecodeArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the list is in LDS for the whole wave
   __builtin_amdgcn_wave_barrier();
-  const int cpt = BC / 64;
+  constexpr int cpt = CPT;
   const int nq = nkept * cpt;
   auto chunk_key0 = [&](int q) { return (u.t0 + list[q / cpt]) * BC + (q % cpt) * 64; };
   auto load_chunk = [&](u32x4 (&vv)[kIt], float (&sv)[GM], int q) {
@@ -867,10 +878,16 @@ hipError_t launch_dg(const DecodeArgs& a, hipStream_t stream) {
     if (a.fused) return launch_fused<D, GM>(a, stream);
   }
   const int units = a.g.B * a.g.Hkv * a.nsplit;
-  hipLaunchKernelGGL((decode_scores<D, GM>), dim3(units), dim3(kDecThreads), 0, stream, a);
+  if (a.block_k == 128)
+    hipLaunchKernelGGL((decode_scores<D, GM, 2>), dim3(units), dim3(kDecThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_scores<D, GM, 1>), dim3(units), dim3(kDecThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_attend<D, GM>), dim3(units), dim3(kDecThreads), 0, stream, a);
+  if (a.block_k == 128)
+    hipLaunchKernelGGL((decode_attend<D, GM, 2>), dim3(units), dim3(kDecThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_attend<D, GM, 1>), dim3(units), dim3(kDecThreads), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine<D>), dim3(a.g.B * a.g.Hq), dim3(64), 0, stream, a);
