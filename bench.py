@@ -615,7 +615,8 @@ def video_variant_leg(c, head, kind):
     if not c.only:
         rec["speedup_vs_lambda0"] = round(rec["lambda0"]["ms"] / rec["calibrated"]["ms"], 3)
         rec["speedup_vs_headline_tile_64"] = round(ms_tile / rec["calibrated"]["ms"], 3)
-    rec["roofline"] = roofline("mfma", rec["calibrated"]["computed_tflops"])
+    rec["roofline"] = roofline("mfma", rec["calibrated"]["computed_tflops"],
+                               f"skip_softmax_video_dit_s32760_{kind}.txt", "skip")
     return rec
 
 
