@@ -34,21 +34,36 @@ import numpy as np
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_DIR, "sa_oracle.c")
-_LIB_PATH = os.path.join(_DIR, "libsa_oracle.so")
+_DEFAULT_LIB = os.path.join(_DIR, "libsa_oracle.so")
+# SA_ORACLE_LIB names another build of the oracle (the sanitizer build, for instance).
+_LIB_PATH = os.environ.get("SA_ORACLE_LIB") or _DEFAULT_LIB
 _lib = None
 
 GCC_FLAGS = ["-O2", "-std=gnu11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
              "-fno-fast-math", "-Wall", "-Wextra"]
 
+# AddressSanitizer + UndefinedBehaviorSanitizer build with ROCm's clang, whose shared ASan runtime
+# the HIP library's sanitizer build uses too (one runtime per process).
+SAN_LIB = os.path.join(_DIR, "libsa_oracle_san.so")
+CLANG = "/opt/rocm/llvm/bin/clang"
+SAN_FLAGS = ["-O1", "-g", "-std=gnu11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+             "-fno-fast-math", "-fsanitize=address,undefined", "-fno-omit-frame-pointer",
+             "-shared-libasan", "-Wl,-rpath,/opt/rocm/llvm/lib"]
 
-def build(force: bool = False) -> str:
-    """Compile sa_oracle.c into libsa_oracle.so with gcc (host code only)."""
-    if force or not os.path.exists(_LIB_PATH) or (
-            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
-        tmp = _LIB_PATH + f".tmp{os.getpid()}"
-        subprocess.run(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"], check=True)
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+
+def build(force: bool = False, sanitize: bool = False) -> str:
+    """Compile sa_oracle.c into libsa_oracle.so with gcc (host code only); with sanitize=True into
+    libsa_oracle_san.so with clang and ASan/UBSan."""
+    out = SAN_LIB if sanitize else _LIB_PATH
+    sanitize = out == SAN_LIB
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(_SRC):
+        if out not in (_DEFAULT_LIB, SAN_LIB):
+            raise RuntimeError(f"{out} (SA_ORACLE_LIB) is missing or older than {_SRC}")
+        tmp = out + f".tmp{os.getpid()}"
+        cmd = [CLANG, *SAN_FLAGS] if sanitize else ["gcc", *GCC_FLAGS]
+        subprocess.run([*cmd, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, out)
+    return out
 
 
 def _load():

@@ -18,7 +18,8 @@ import os
 import torch
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_DIR, "libsa_hip.so")
+# SA_HIP_LIB names another build of the same library (the host-sanitizer build, for instance).
+LIB_PATH = os.environ.get("SA_HIP_LIB") or os.path.join(_DIR, "libsa_hip.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python sparse_attention_flash_amd/build.py`")

@@ -42,15 +42,26 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libsa_hip.so; returns the library path."""
-    objdir = os.path.join(PKG, "_build")
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build (libsa_hip_san.so): the C ABI's
+# argument checks, planning and launch code run instrumented; device code is built as usual.  The
+# shared ASan runtime must be preloaded into the host process (tests/run_cpu_tests_sanitized.sh).
+SAN_LIB_NAME = "libsa_hip_san.so"
+SAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile every HIP source and link libsa_hip.so (libsa_hip_san.so with sanitize=True);
+    returns the library path."""
+    objdir = os.path.join(PKG, "_build_san" if sanitize else "_build")
+    lib_path = os.path.join(PKG, SAN_LIB_NAME) if sanitize else LIB_PATH
+    extra = SAN_HOST_FLAGS if sanitize else []
     os.makedirs(objdir, exist_ok=True)
     objs = []
     procs = []
     for src in sources():
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+        cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
         procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE,
                                                  stderr=subprocess.STDOUT)))
         objs.append(obj)
@@ -67,14 +78,15 @@ def build(verbose: bool = False) -> str:
     if failed:
         msg = "\n".join(f"--- {s}\n{t}" for s, t in failed)
         raise RuntimeError(f"hipcc failed:\n{msg}")
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
-    subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
-                   check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    tmp = lib_path + f".tmp{os.getpid()}"
+    link_extra = [*extra, "-shared-libasan"] if sanitize else []
+    subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, *objs,
+                    "-o", tmp], check=True)
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
     t0 = time.time()
-    path = build(verbose="-v" in sys.argv)
+    path = build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv)
     print(f"built {path} in {time.time() - t0:.1f}s")
