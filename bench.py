@@ -4,6 +4,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-paths]
     python bench.py --only LEG [--steps K] [--warmup W]       (one leg, for profiler runs)
     python bench.py --cpu-full-runs                           (the oracle's full-run times)
+    python bench.py --peak-probes                             (attainable HBM / GEMM rates)
 
 One step is one pass of the skip-softmax hot path over the headline workload: the calibrated
 threshold lowering (host, a*exp(b*0.5)/seq_k) followed by the skip-softmax forward with its tile
@@ -61,10 +62,41 @@ def parse_args(argv=None):
     p.add_argument("--cpu-full-runs", action="store_true",
                    help="time the CPU oracle over the whole of the small, causal-GQA, N:M and "
                         "proxy workloads (minutes of CPU time) and print the times")
+    p.add_argument("--peak-probes", action="store_true",
+                   help="only measure the attainable HBM read / copy rates and a library bf16 "
+                        "GEMM rate on this part, and print them")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="only run 5 device-to-device copies of BYTES bytes (a plain copy kernel "
                         "of known size, used to scale the HBM byte counters) and exit")
     return p.parse_args(argv)
+
+
+def peak_probes():
+    """Attainable rates on this part, for the roofline's context (the roofline itself uses the
+    published peaks): an HBM read stream (a sum over 4 GiB of seeded random data, larger than the
+    256 MB last-level cache, so nothing is served from it), a read+write stream (a copy of 1 GiB,
+    counting both directions), and a library bf16 GEMM (torch.matmul, 8192^3, hipBLASLt)."""
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    out = {}
+    x = torch.rand(1 << 30, generator=g, device=dev)             # 4 GiB fp32
+    ms = time_steps(torch, lambda: x.sum(), 10, 3)
+    out["read_stream_gbps"] = round(x.numel() * 4 / ms / 1e6, 1)
+    del x
+    a = torch.rand(1 << 28, generator=g, device=dev)             # 1 GiB
+    b = torch.empty_like(a)
+    ms = time_steps(torch, lambda: b.copy_(a), 10, 3)
+    out["copy_read_plus_write_gbps"] = round(2 * a.numel() * 4 / ms / 1e6, 1)
+    del a, b
+    n = 8192
+    ma = torch.randn(n, n, generator=g, device=dev).to(torch.bfloat16)
+    mb = torch.randn(n, n, generator=g, device=dev).to(torch.bfloat16)
+    ms = time_steps(torch, lambda: torch.matmul(ma, mb), 20, 5)
+    out["bf16_gemm_8192_tflops"] = round(2 * n ** 3 / ms / 1e9, 1)
+    torch.cuda.empty_cache()
+    return out
 
 
 def copy_probe(nbytes):
@@ -686,6 +718,9 @@ def main(argv=None):
         sys.exit(2)
     if args.cpu_full_runs:
         print(json.dumps(cpu_full_runs()))
+        return
+    if args.peak_probes:
+        print(json.dumps(peak_probes()))
         return
     if args.copy_probe:
         copy_probe(args.copy_probe)
