@@ -70,8 +70,56 @@ namespace {
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// P.V of one 64-key chunk for the heads of a KV head, on the VALU (a rank-GM update with no
+// contraction depth to fill an MFMA).  A V row is D/8 lanes of 16 bytes; lane (sub, c) loads keys
+// sub + KPI*it (it < kIt) at d = 8c..8c+7.  Keys sub + KPI*2j and sub + KPI*(2j+1) are paired:
+// v_perm_b32 puts their values at one d into one word and v_dot2_f32_bf16 adds both products to
+// the fp32 accumulator, half the instructions of a multiply-add per key.  P goes through LDS as
+// bf16 (as in the prefill P.V), in the pairing's layout: word [pair][h] holds head h's P of the
+// pair's first key in its low half and of its second key in its high half.
+template <int D, int GM>
+struct PvChunk {
+  static constexpr int LPK = D / 8;       // lanes per V row
+  static constexpr int KPI = 64 / LPK;    // keys per load instruction
+  static constexpr int kIt = 64 / KPI;    // load instructions per chunk
+  static constexpr int GQ = (GM + 3) / 4; // 16-byte groups of heads
+  static constexpr int kPairs = 32;
+  typedef uint32_t Buf[kPairs][4 * GQ];
+
+  // lane = key kl of the chunk writes its heads' P (p[h] for h < 4*GQ, zero past the group)
+  static __device__ __forceinline__ void write_p(Buf& pw, int kl, const float (&p)[4 * GQ]) {
+    const int it = kl / KPI, sub = kl % KPI;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(&pw[sub + KPI * (it >> 1)][0]) + (it & 1);
+#pragma unroll
+    for (int h = 0; h < 4 * GQ; ++h) dst[2 * h] = __builtin_bit_cast(uint16_t, (__bf16)p[h]);
+  }
+
+  static __device__ __forceinline__ void accumulate(const Buf& pw, const u32x4 (&vv)[kIt], int sub,
+                                                    float (&acc)[GM][8]) {
+#pragma unroll
+    for (int j = 0; j < kIt / 2; ++j) {
+      uint32_t pp[4 * GQ];
+#pragma unroll
+      for (int q4 = 0; q4 < GQ; ++q4) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(&pw[sub + KPI * j][4 * q4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pp[4 * q4 + e] = w[e];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w1 = vv[2 * j][i], w2 = vv[2 * j + 1][i];
+        const bf16x2 lo = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(w2, w1, 0x05040100u));
+        const bf16x2 hi = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(w2, w1, 0x07060302u));
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+          const bf16x2 ph = __builtin_bit_cast(bf16x2, pp[h]);
+          acc[h][2 * i] = __builtin_amdgcn_fdot2_f32_bf16(lo, ph, acc[h][2 * i], false);
+          acc[h][2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(hi, ph, acc[h][2 * i + 1], false);
+        }
+      }
+    }
+  }
+};
 
 // The (batch, KV head, split) of this workgroup and its key range.
 struct DecUnit {
@@ -369,7 +417,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attend(DecodeArgs a) {
   __shared__ float ref_s[GM];
   __shared__ uint32_t keepbits[kMaxTilesPerSplit];
   __shared__ float stage[GM][64];
-  __shared__ __attribute__((aligned(16))) float pbuf[kDecWaves][64][4 * GQ];
+  __shared__ __attribute__((aligned(16))) typename PvChunk<D, GM>::Buf pbuf[kDecWaves];
   __shared__ uint16_t klist[kDecWaves][kMaxTilesPerSplit / kDecWaves];
   __shared__ float red[kDecWaves][GM][D];
   __shared__ float lred[kDecWaves][GM];
@@ -403,7 +451,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attend(DecodeArgs a) {
   const int vstride_b = (int)(g.vs[1] * 2);
   const int64_t row_len = (int64_t)a.nKT * BC;   // scores row stride
   const float* sc = a.scores + ((int64_t)u.b * g.Hkv + u.hk) * GM * row_len;
-  float (*pw)[4 * GQ] = pbuf[wave];
+  typename PvChunk<D, GM>::Buf& pw = pbuf[wave];
 
   // This wave's kept tiles t = t0 + wave + kDecWaves*i (kept by some head) listed in LDS, then
   // walked as 64-key chunks; the V rows and scores of chunk q+1 are loaded while chunk q is
@@ -436,38 +484,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_attend(DecodeArgs a) {
     const uint32_t kb = keepbits[key0 / BC - u.t0];
     // P of the 64 keys, one key per lane, into this wave's LDS slot; l from the same values
     const bool valid = key0 + lane < u.len;
+    float p[4 * GQ];
 #pragma unroll
     for (int h = 0; h < 4 * GQ; ++h) {
-      float p = 0.f;
+      p[h] = 0.f;
       if (h < GM && ((kb >> h) & 1u) && valid)
-        p = __builtin_amdgcn_exp2f(sv[h < GM ? h : 0] * g.c32 - ref[h < GM ? h : 0]);
-      if (h < GM) ls[h] += p;
-      pw[lane][h] = p;
+        p[h] = __builtin_amdgcn_exp2f(sv[h < GM ? h : 0] * g.c32 - ref[h < GM ? h : 0]);
+      if (h < GM) ls[h] += p[h];
     }
+    PvChunk<D, GM>::write_p(pw, lane, p);
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): P is in LDS for the whole wave
     __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int kl = sub + it * KPI;   // key within the 64
-      float vf[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w = vv[it][i];
-        vf[2 * i] = bf16_lo(w);
-        vf[2 * i + 1] = bf16_hi(w);
-      }
-#pragma unroll
-      for (int q4 = 0; q4 < GQ; ++q4) {
-        const f32x4 p4 = *(const f32x4*)&pw[kl][4 * q4];
-#pragma unroll
-        for (int hh = 0; hh < 4; ++hh) {
-          const int h = 4 * q4 + hh;
-          if (h >= GM) break;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] += p4[hh] * vf[e];
-        }
-      }
-    }
+    PvChunk<D, GM>::accumulate(pw, vv, sub, acc);
     __builtin_amdgcn_wave_barrier();   // every lane has read P before the next chunk rewrites it
   };
   if (nq > 0) {
@@ -594,7 +622,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused(DecodeArgs a) {
   __shared__ uint16_t klist[kMaxChunks];    // tiles kept by some head, ascending
   __shared__ int nkept_s;
   __shared__ float ref_s[GM];
-  __shared__ __attribute__((aligned(16))) float pbuf[kFusedWaves][64][4 * GQ];
+  __shared__ __attribute__((aligned(16))) typename PvChunk<D, GM>::Buf pbuf[kFusedWaves];
   __shared__ float lred[kFusedWaves][GM];
 
   for (int t = tid; t < nKT; t += kFusedThreads) kbits[t] = 0u;
@@ -763,7 +791,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused(DecodeArgs a) {
     const __bf16* vslab = (const __bf16*)g.v + b * g.vs[0] + hk * g.vs[2];
     const auto vrs = slab_rsrc(vslab, g.vs[1], len, D);
     const int vstride_b = (int)(g.vs[1] * 2);
-    float (*pw)[4 * GQ] = pbuf[wave];
+    typename PvChunk<D, GM>::Buf& pw = pbuf[wave];
     const int nq_all = nkept_s * cpt;
     const int nq = nq_all > wave ? (nq_all - wave + kFusedWaves - 1) / kFusedWaves : 0;
     auto chunk_of = [&](int i) { return wave + kFusedWaves * i; };   // index into the kept chunks
@@ -783,39 +811,19 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused(DecodeArgs a) {
       const uint32_t kb = kbits[klist[q / cpt]];
       // P of the 64 keys, one key per lane, into this wave's LDS slot; l from the same values
       const bool valid = key0 + lane < len;
+      float p[4 * GQ];
 #pragma unroll
       for (int h = 0; h < 4 * GQ; ++h) {
-        float p = 0.f;
+        p[h] = 0.f;
         if (h < G && ((kb >> h) & 1u) && valid)
-          p = __builtin_amdgcn_exp2f(sc[(h < GM ? h : 0) * row_len + key0 + lane] * g.c32 -
-                                     ref[h < GM ? h : 0]);
-        if (h < GM) ls[h < GM ? h : 0] += p;
-        pw[lane][h] = p;
+          p[h] = __builtin_amdgcn_exp2f(sc[(h < GM ? h : 0) * row_len + key0 + lane] * g.c32 -
+                                        ref[h < GM ? h : 0]);
+        if (h < GM) ls[h < GM ? h : 0] += p[h];
       }
+      PvChunk<D, GM>::write_p(pw, lane, p);
       __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): P is in LDS for the whole wave
       __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int it = 0; it < kIt; ++it) {
-        const int kl = sub + it * KPI;   // key within the 64
-        float vf[8];
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const uint32_t w = vv[it][i4];
-          vf[2 * i4] = bf16_lo(w);
-          vf[2 * i4 + 1] = bf16_hi(w);
-        }
-#pragma unroll
-        for (int q4 = 0; q4 < GQ; ++q4) {
-          const f32x4 p4 = *(const f32x4*)&pw[kl][4 * q4];
-#pragma unroll
-          for (int hh = 0; hh < 4; ++hh) {
-            const int h = 4 * q4 + hh;
-            if (h >= GM) break;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] += p4[hh] * vf[e];
-          }
-        }
-      }
+      PvChunk<D, GM>::accumulate(pw, vv, sub, acc);
       __builtin_amdgcn_wave_barrier();   // every lane has read P before the next chunk rewrites it
     };
     if (nq > 0) {
