@@ -203,7 +203,7 @@ KERNEL_SOURCES = {
     "nm": [_C + "nm_softmax.hip"] + _COMMON,
     "skip_nm": [_C + "skip_nm_softmax.hip"] + _COMMON,
     "proxy": [_C + "proxy.hip", _C + "tile_core.h", _C + "mainloop.h", _C + "kernels.h"],
-    "decode": [_C + "decode.hip", _C + "tile_core.h", _C + "kernels.h"],
+    "decode": [_C + "decode.hip", _C + "tile_core.h", _C + "mainloop.h", _C + "kernels.h"],
 }
 SKIP_SOURCES = KERNEL_SOURCES["skip"]
 DECODE_PROFILE_LAMBDA = 0.1146   # decode workload: target 0.5 lowered through its own fit
