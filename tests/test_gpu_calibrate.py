@@ -69,3 +69,31 @@ def test_calibration_sweep_and_fit():
     got = sa.sa_skip_softmax_calibrate(qd, kd, vd, o, [lam_t], cnt, block_q=Br)[0]
     announce(f"fit a={a:.4g} b={b:.4g} range [{lo:.3f}, {hi:.3f}]; target {target:.3f} -> {got:.3f}")
     assert abs(got - target) < 0.15
+
+
+def test_calibration_sweep_at_128_key_tiles():
+    """The sweep at the pages' 128 x 128 tiles (Model-Optimizer HuggingFace page, "Custom
+    Configuration"): each trial's sparsity is the tile_state histogram of the forward kernel at
+    block_k = 128, and the oracle's float64 decisions on 128-key tiles agree to within 0.1 % of the
+    visited tiles."""
+    announce("calibration sweep at 128 x 128 tiles")
+    q, k, v = W.gen_video(7, 1, 2, 128, grid=(5, 16, 26))
+    B, S, H, D = q.shape
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o = torch.empty((B, S, H, D), dtype=torch.bfloat16, device="cuda")
+    cnt = torch.zeros((B, H, 2), dtype=torch.int32, device="cuda")
+    trials = _trials()
+    sp = sa.sa_skip_softmax_calibrate(qd, kd, vd, o, trials, cnt, block_q=128, block_k=128)
+    assert all(b >= a for a, b in zip(sp, sp[1:])), sp
+    assert 0.0 < max(sp) < 1.0   # the sweep reaches sparsity on this input
+    nQT, nKT = sa.tile_counts(S, S, 128, 128)
+    for lam, s in zip(trials, sp):
+        st = torch.full((B, H, nQT, nKT), 255, dtype=torch.uint8, device="cuda")
+        sa.sa_skip_softmax_fwd(qd, kd, vd, o, lam, block_q=128, block_k=128, tile_state=st)
+        torch.cuda.synchronize()
+        st = st.cpu().numpy()
+        visited = int((st != 2).sum())
+        assert s == (st == 1).sum() / visited
+        _, _, st_ref, _ = oracle.skip_softmax(q, k, v, causal=False, block_q=128, block_k=128,
+                                              scale=1 / math.sqrt(D), lam=lam)
+        assert abs(int((st_ref == 1).sum()) - int((st == 1).sum())) <= max(1, visited // 1000)
