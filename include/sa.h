@@ -196,7 +196,11 @@ sa_status sa_skip_nm_softmax_fwd(const sa_attn_desc* desc, const void* q, const 
  *   lse               optional fp32 [B, Hq].
  *   dbg_tile_rowmax   optional fp32 [B, Hq, nKT]: the M_j used (log2 domain), -inf when not
  *                     visited.
- * Three kernels on the stream: scores and tile maxima, decisions and P.V over kept tiles, merge.
+ * Kernels on the stream: when the call runs one split (num_splits 1, or num_splits 0 with
+ * lambda > 1) and the head group's scores over the whole cache fit in 128 KiB, one kernel with one
+ * workgroup per (batch, KV head) keeps them in LDS (the workspace is then not touched, though a
+ * buffer of the queried size is still required); otherwise three: scores and tile maxima,
+ * decisions and P.V over kept tiles, merge of the splits.
  */
 sa_status sa_skip_softmax_decode_workspace(const sa_attn_desc* desc, float lambda,
                                            int32_t num_splits, size_t* workspace_bytes,
