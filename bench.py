@@ -90,13 +90,23 @@ def peak_probes():
     ms = time_steps(torch, lambda: b.copy_(a), 10, 3)
     out["copy_read_plus_write_gbps"] = round(2 * a.numel() * 4 / ms / 1e6, 1)
     del a, b
+    out["bf16_gemm_8192_tflops"] = gemm_probe(torch)
+    torch.cuda.empty_cache()
+    return out
+
+
+def gemm_probe(torch):
+    """TFLOP/s of torch.matmul (hipBLASLt) on two 8192 x 8192 bf16 matrices: the part's own
+    library bf16 GEMM rate."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
     n = 8192
     ma = torch.randn(n, n, generator=g, device=dev).to(torch.bfloat16)
     mb = torch.randn(n, n, generator=g, device=dev).to(torch.bfloat16)
     ms = time_steps(torch, lambda: torch.matmul(ma, mb), 20, 5)
-    out["bf16_gemm_8192_tflops"] = round(2 * n ** 3 / ms / 1e9, 1)
-    torch.cuda.empty_cache()
-    return out
+    del ma, mb
+    return round(2 * n ** 3 / ms / 1e9, 1)
 
 
 def copy_probe(nbytes):
@@ -844,6 +854,11 @@ def main(argv=None):
             "wrapper_ms_off_on": [1.3172, 1.4298], "attention_ms_off_on": [1.1261, 1.2121],
             "prep_ms_off_on": [0.0145, 0.0176]}
         result["paths"] = paths
+        # the part's library bf16 GEMM in the same run (same lease, clocks and thermals), as a
+        # reference point for the headline's rate; not part of the roofline
+        gemm = gemm_probe(torch)
+        result["same_run_reference"] = {"hipblaslt_bf16_gemm_8192_tflops": gemm,
+                                        "headline_over_gemm": round(tflops / gemm, 3)}
     if not args.no_cpu_baseline and not only:
         result["cpu_baseline"] = cpu_baseline(q, k, v, wl, lam, P, args.cpu_seconds)
     print(json.dumps(result))
