@@ -275,7 +275,9 @@ def _fp32_closed_form_states(rm32, Sq, Br, Bc, causal, lam):
 
 @pytest.mark.parametrize("lam", [0.1, 0.4, 0.8, 1.0])
 @pytest.mark.parametrize("causal,Sq,Br,Bc", [(True, 512, 128, 64), (False, 300, 64, 64),
-                                             (True, 200, 32, 128), (False, 257, 32, 64)])
+                                             (True, 200, 32, 128), (False, 257, 32, 64),
+                                             # the last query row is the first key of a tile
+                                             (True, 257, 64, 64), (True, 129, 128, 128)])
 def test_skip_replay_matches_fp32_closed_form(lam, causal, Sq, Br, Bc):
     """Replay from maxima of numpy fp32 logits equals the fp32 closed form (lambda <= 1)."""
     D, H = 64, 3
@@ -298,6 +300,26 @@ def test_skip_replay_matches_fp32_closed_form(lam, causal, Sq, Br, Bc):
     vis = st != 2
     if (causal, Sq, Br, Bc) == (False, 257, 32, 64):   # not vacuous: this case skips 22-67 tiles
         assert (st[vis] == 1).sum() >= 20
+
+
+def test_skip_replay_threshold_is_rounded_to_fp32():
+    """The threshold is fl32(m + L32), not the exact sum: with a running max m for which the fp32
+    sum rounds down, a tile whose max equals fl32(m + L32) is kept (the exact sum would skip it).
+    Inside one binade of m the bits of the sum below m's last place come from L32 alone, so the
+    case is searched over lambda and the binade of m."""
+    def find():
+        for lam in np.linspace(0.3, 0.95, 14):
+            L32 = np.float32(math.log2(np.float64(np.float32(lam))))
+            for m in (np.float32(3.0), np.float32(5.0), np.float32(10.0), np.float32(20.0)):
+                thr = np.float32(m + L32)
+                if np.float64(thr) < np.float64(m) + np.float64(L32):
+                    return float(lam), m, thr
+        raise AssertionError("no rounding-down case")
+    lam, m, thr = find()
+    rm = np.array([[[m], [thr], [np.nextafter(thr, np.float32(-np.inf))]]], np.float32)
+    st = oracle.skip_replay(rm, batch=1, heads_q=1, seqlen_q=1, seqlen_k=3, causal=False,
+                            block_q=1, block_k=1, lam=lam)
+    assert st[0].tolist() == [0, 0, 1]
 
 
 @pytest.mark.parametrize("lam,state", [(0.0, [0, 0, 0, 0]), (2.0, [0, 0, 1, 0]),
