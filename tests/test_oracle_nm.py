@@ -154,9 +154,12 @@ def test_rejects_bad_arguments():
 
 @pytest.mark.parametrize("n,m", NM_PAIRS + [(4, 4), (8, 8)])
 @pytest.mark.parametrize("causal", [True, False])
-def test_keep_replay_matches_argsort(n, m, causal):
-    """Keep bits from fp32 scores equal a numpy stable-argsort top-n over the same scores."""
-    Sq, Hq, D, sink, recent = 150, 2, 32, 3, 9
+@pytest.mark.parametrize("sink,recent", [(3, 9), (0, 0)])
+def test_keep_replay_matches_argsort(n, m, causal, sink, recent):
+    """Keep bits from fp32 scores equal a numpy stable-argsort top-n over the same scores.  With
+    no windows (0, 0) the group holding the diagonal is ranked too, which checks the causal mask
+    of the replay's own inputs (a window of M or more keys keeps that whole group dense)."""
+    Sq, Hq, D = 150, 2, 32
     q, k, _ = W.gen_llm(41, 1, Sq, Hq, Hq, D)
     s32 = refs.scores(q, k).astype(np.float32)[0]               # [H, Sq, Sk]
     allowed = np.tril(np.ones((Sq, Sq), bool)) if causal else np.ones((Sq, Sq), bool)
