@@ -100,6 +100,24 @@ def test_bsr_route_rows_are_sets():
         assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("indptr,indices,exact", [
+    ([0, 3], [1, 1, 4], [1, 4]),     # ascending, one entry repeated
+    ([0, 2], [2, 8], [2]),           # ascending, the last entry one past the final block
+    ([0, 2], [-1, 3], [3]),          # ascending, a negative entry
+    ([0, 2], [5, 2], [2, 5]),        # distinct and in range, but descending
+    ([-1, 2], [3, 6], [3, 6]),       # a negative start pointer, clamped to 0
+])
+def test_bsr_route_each_defect_alone_makes_the_row_non_canonical(indptr, indices, exact):
+    # "Bitmask format": a canonical row is strictly ascending and in range, so each defect on its
+    # own is counted, while the route is that of the set the row names.
+    got = oracle.bsr_route_prep(np.array(indptr, np.int32), np.array(indices, np.int32), 8)
+    ref = oracle.bsr_route_prep(np.array([0, len(exact)], np.int32), np.array(exact, np.int32), 8)
+    assert got[3] == 1 and ref[3] == 0
+    assert got[0].tolist() == [len(exact)] and got[1][0, :len(exact)].tolist() == exact
+    for x, y in zip(ref[:3], got[:3]):
+        assert np.array_equal(x, y)
+
+
 def test_bsr_route_bad_pointers_are_clamped():
     # A reversed pointer pair is an empty row; a range past nnz is cut at nnz.  Both are counted.
     indptr = np.array([0, 2, 1, 4], np.int32)

@@ -109,6 +109,51 @@ def test_replay_and_forced_modes_reproduce_their_inputs():
     assert np.abs(o2 - o).max() < 1e-12
 
 
+@pytest.mark.parametrize("case", CASES)
+def test_replay_mode_decides_from_the_given_maxima_alone(case):
+    """Mode 1 decides from the fp32 maxima it is handed, exactly as the separately pinned
+    decisions-only replay does: on maxima that are not the true ones (perturbed), the two agree on
+    every tile, while the keep bits still come from the given scores."""
+    B, S, Hq, Hkv, D, causal, Br, Bc, n, m, sink, recent = case
+    q, k, v = _inputs(66, case)
+    _, _, _, rm, kb = _combined(q, k, v, case, 0.0)
+    rm32 = rm.astype(np.float32)
+    fin = np.isfinite(rm32)
+    rm32[fin] += np.random.default_rng(67).normal(0, 0.5, int(fin.sum())).astype(np.float32)
+    sc = refs.scores(q, k).astype(np.float32)
+    nQT, nKT = rm.shape[2], rm.shape[3]
+    skipped = 0
+    for lam in (0.5, 1.0, 3.0):
+        _, _, st, _, kb1 = _combined(q, k, v, case, lam, mode=1, rowmax_in=rm32, scores_in=sc)
+        ref = oracle.skip_replay(rm32.reshape(-1, nKT, Br), batch=B, heads_q=Hq, seqlen_q=S,
+                                 seqlen_k=S, causal=causal, block_q=Br, block_k=Bc, lam=lam)
+        assert np.array_equal(st.reshape(-1, nKT), ref)
+        assert np.array_equal(kb1, kb)
+        skipped += int((ref == 1).sum())
+    assert skipped > 0
+
+
+def test_replay_mode_threshold_is_rounded_to_fp32():
+    """As in the skip-softmax replay: the threshold is fl32(m + L32), so with a running max m for
+    which that sum rounds down, a tile whose max equals it is kept and one just below is skipped."""
+    def find():
+        for lam in np.linspace(0.3, 0.95, 14):
+            L32 = np.float32(math.log2(np.float64(np.float32(lam))))
+            for m in (np.float32(3.0), np.float32(5.0), np.float32(10.0), np.float32(20.0)):
+                thr = np.float32(m + L32)
+                if np.float64(thr) < np.float64(m) + np.float64(L32):
+                    return float(lam), m, thr
+        raise AssertionError("no rounding-down case")
+    lam, m, thr = find()
+    q, k, v = W.gen_iid(68, 1, 1, 3, 1, 1, 16)
+    rm = np.array([m, thr, np.nextafter(thr, np.float32(-np.inf))], np.float32)
+    _, _, st, _, _ = oracle.skip_nm_softmax(q, k, v, causal=False, block_q=1, block_k=1,
+                                            scale=0.25, lam=lam, n=1, m=1, sink=0, recent=0,
+                                            mode=1, rowmax_in=rm,
+                                            scores_in=np.zeros((1, 1, 1, 3), np.float32))
+    assert st.ravel().tolist() == [0, 0, 1]
+
+
 def test_rejects_bad_arguments():
     q, k, v = W.gen_iid(65, 1, 64, 64, 1, 1, 16)
     with pytest.raises(ValueError):
