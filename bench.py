@@ -73,18 +73,60 @@ def parse_args(argv=None):
 
 def peak_probes():
     """Attainable rates on this part, for the roofline's context (the roofline itself uses the
-    published peaks): an HBM read stream (a sum over 4 GiB of seeded random data, larger than the
-    256 MB last-level cache, so nothing is served from it), a read+write stream (a copy of 1 GiB,
-    counting both directions), and a library bf16 GEMM (torch.matmul, 8192^3, hipBLASLt)."""
+    published peaks), from libsa_probes.so (include/sa_probes.h) and torch:
+      * the bf16 matrix-core rate: four independent v_mfma_f32_32x32x16_bf16 chains per wave,
+        16 waves per CU, register operands only, once with random operands that change from
+        issue to issue (the switching power of real data) and once with constant ones;
+      * the HBM read rate: 16 KiB contiguous chunks, four in flight per wave, over four 268 MB
+        buffers read in rotation (1.07 GB in all, more than the 256 MB last-level cache, so no
+        launch finds its data there);
+      * a read+write stream (torch copy of 1 GiB, both directions counted);
+      * a library bf16 GEMM (torch.matmul, 8192^3, hipBLASLt)."""
+    import ctypes
     import torch
+    path = os.path.join(ROOT, "sparse_attention_flash_amd", "libsa_probes.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with sparse_attention_flash_amd/build.py")
+    lib = ctypes.CDLL(path)
+    lib.sa_probe_mfma_bf16_flops.restype = ctypes.c_double
+    lib.sa_probe_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.sa_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p]
+    lib.sa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_void_p]
     dev = torch.device("cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = {}
+
+    wgs, iters = 1024, 20000
+    buf = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+
+    for key, rnd in (("mfma_bf16_tflops_random_operands", 1),
+                     ("mfma_bf16_tflops_constant_operands", 0)):
+        def mfma():
+            if lib.sa_probe_mfma_bf16(ctypes.c_void_p(buf.data_ptr()), wgs, iters, rnd, stream):
+                raise RuntimeError("sa_probe_mfma_bf16 failed")
+        ms = time_steps(torch, mfma, 10, 3)
+        out[key] = round(lib.sa_probe_mfma_bf16_flops(wgs, iters) / ms / 1e9, 1)
+
     g = torch.Generator(device=dev)
     g.manual_seed(0)
-    out = {}
-    x = torch.rand(1 << 30, generator=g, device=dev)             # 4 GiB fp32
-    ms = time_steps(torch, lambda: x.sum(), 10, 3)
-    out["read_stream_gbps"] = round(x.numel() * 4 / ms / 1e6, 1)
-    del x
+    nbytes, rwgs = 1 << 28, 512
+    bufs = [torch.randint(0, 1 << 15, (nbytes // 2,), generator=g, dtype=torch.int16, device=dev)
+            for _ in range(4)]
+    sink = torch.empty(rwgs * 512, dtype=torch.int32, device=dev)
+    turn = [0]
+
+    def read():
+        x = bufs[turn[0] % len(bufs)]
+        turn[0] += 1
+        if lib.sa_probe_read(ctypes.c_void_p(x.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                             rwgs, stream) != 0:
+            raise RuntimeError("sa_probe_read failed")
+    ms = time_steps(torch, read, 12, 4)
+    out["read_stream_gbps"] = round(nbytes / ms / 1e6, 1)
+    del bufs, sink
+
     a = torch.rand(1 << 28, generator=g, device=dev)             # 1 GiB
     b = torch.empty_like(a)
     ms = time_steps(torch, lambda: b.copy_(a), 10, 3)

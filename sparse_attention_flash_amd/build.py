@@ -3,7 +3,8 @@
     python sparse_attention_flash_amd/build.py
 
 Every ``csrc/*.hip`` file is compiled for gfx950 only and linked into one shared library next to
-this file.  Packed-fp32 instruction selection is disabled for all device code.
+this file, and ``probes/*.hip`` (the peak-rate microbenchmarks of include/sa_probes.h) into
+libsa_probes.so beside it.  Packed-fp32 instruction selection is disabled for all device code.
 """
 from __future__ import annotations
 
@@ -20,6 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libsa_hip.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+PROBES_LIB_PATH = os.path.join(PKG, "libsa_probes.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -51,15 +53,23 @@ SAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitiz
 
 
 def build(verbose: bool = False, sanitize: bool = False) -> str:
-    """Compile every HIP source and link libsa_hip.so (libsa_hip_san.so with sanitize=True);
-    returns the library path."""
-    objdir = os.path.join(PKG, "_build_san" if sanitize else "_build")
+    """Compile every HIP source and link libsa_hip.so (libsa_hip_san.so with sanitize=True), and
+    libsa_probes.so unless sanitizing; returns the attention library's path."""
     lib_path = os.path.join(PKG, SAN_LIB_NAME) if sanitize else LIB_PATH
+    _link(sources(), "_build_san" if sanitize else "_build", lib_path, sanitize, verbose)
+    if not sanitize:
+        _link(sorted(glob.glob(os.path.join(PKG, "probes", "*.hip"))), "_build_probes",
+              PROBES_LIB_PATH, False, verbose)
+    return lib_path
+
+
+def _link(srcs, objdir_name, lib_path, sanitize, verbose):
+    objdir = os.path.join(PKG, objdir_name)
     extra = SAN_HOST_FLAGS if sanitize else []
     os.makedirs(objdir, exist_ok=True)
     objs = []
     procs = []
-    for src in sources():
+    for src in srcs:
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
         procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE,
@@ -83,7 +93,6 @@ def build(verbose: bool = False, sanitize: bool = False) -> str:
     subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, *objs,
                     "-o", tmp], check=True)
     os.replace(tmp, lib_path)
-    return lib_path
 
 
 if __name__ == "__main__":

@@ -18,8 +18,8 @@ FAKE = 0x10000          # 16-byte aligned dummy address, never dereferenced
 FAKE_MIS = 0x10008      # misaligned dummy address
 
 
-def declared_entry_points():
-    text = open(os.path.join(ROOT, "include", "sa.h")).read()
+def declared_entry_points(header="sa.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(sa_[a-z0-9_]+)\s*\(", text)))
 
@@ -34,6 +34,28 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(sa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_probe_library_exports_its_header_and_rejects_bad_arguments():
+    """libsa_probes.so (the peak-rate microbenchmarks bench.py --peak-probes runs) exports what
+    sa_probes.h declares, and rejects bad arguments on the host before any launch."""
+    names = declared_entry_points("sa_probes.h")
+    assert names == ["sa_probe_mfma_bf16", "sa_probe_mfma_bf16_flops", "sa_probe_read"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_attention_flash_amd", "libsa_probes.so"))
+    for n in names:
+        assert hasattr(lib, n), n
+    lib.sa_probe_mfma_bf16_flops.restype = ctypes.c_double
+    assert lib.sa_probe_mfma_bf16_flops(3, 5) == 3 * 4 * 5 * 4 * 32768
+    V, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.sa_probe_mfma_bf16.argtypes = [V, I, I, I, V]
+    lib.sa_probe_read.argtypes = [V, Z, V, I, V]
+    assert lib.sa_probe_mfma_bf16(None, 1, 1, 1, None) == 1
+    assert lib.sa_probe_mfma_bf16(FAKE, 0, 1, 1, None) == 1
+    assert lib.sa_probe_mfma_bf16(FAKE, 1, 0, 0, None) == 1
+    assert lib.sa_probe_read(FAKE, 16384 + 16, FAKE, 1, None) == 1    # not whole chunks
+    assert lib.sa_probe_read(FAKE, 0, FAKE, 1, None) == 1
+    assert lib.sa_probe_read(FAKE_MIS, 16384, FAKE, 1, None) == 1     # misaligned
+    assert lib.sa_probe_read(FAKE, 16384, FAKE, 0, None) == 1
 
 
 def test_status_strings():
