@@ -84,30 +84,13 @@ def peak_probes():
       * a library bf16 GEMM (torch.matmul, 8192^3, hipBLASLt)."""
     import ctypes
     import torch
-    path = os.path.join(ROOT, "sparse_attention_flash_amd", "libsa_probes.so")
-    if not os.path.exists(path):
-        raise RuntimeError(f"{path} is missing: build it with sparse_attention_flash_amd/build.py")
-    lib = ctypes.CDLL(path)
-    lib.sa_probe_mfma_bf16_flops.restype = ctypes.c_double
-    lib.sa_probe_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
-    lib.sa_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                       ctypes.c_void_p]
-    lib.sa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
-                                  ctypes.c_void_p]
+    lib = probe_lib()
     dev = torch.device("cuda:0")
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    out = {}
-
-    wgs, iters = 1024, 20000
-    buf = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
-
-    for key, rnd in (("mfma_bf16_tflops_random_operands", 1),
-                     ("mfma_bf16_tflops_constant_operands", 0)):
-        def mfma():
-            if lib.sa_probe_mfma_bf16(ctypes.c_void_p(buf.data_ptr()), wgs, iters, rnd, stream):
-                raise RuntimeError("sa_probe_mfma_bf16 failed")
-        ms = time_steps(torch, mfma, 10, 3)
-        out[key] = round(lib.sa_probe_mfma_bf16_flops(wgs, iters) / ms / 1e9, 1)
+    out = {
+        "mfma_bf16_tflops_random_operands": mfma_probe(torch, lib, True),
+        "mfma_bf16_tflops_constant_operands": mfma_probe(torch, lib, False),
+    }
 
     g = torch.Generator(device=dev)
     g.manual_seed(0)
@@ -135,6 +118,38 @@ def peak_probes():
     out["bf16_gemm_8192_tflops"] = gemm_probe(torch)
     torch.cuda.empty_cache()
     return out
+
+
+def probe_lib():
+    """libsa_probes.so (include/sa_probes.h), with its ctypes signatures."""
+    import ctypes
+    path = os.path.join(ROOT, "sparse_attention_flash_amd", "libsa_probes.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with sparse_attention_flash_amd/build.py")
+    lib = ctypes.CDLL(path)
+    lib.sa_probe_mfma_bf16_flops.restype = ctypes.c_double
+    lib.sa_probe_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.sa_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p]
+    lib.sa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_void_p]
+    return lib
+
+
+def mfma_probe(torch, lib, random_operands):
+    """TFLOP/s of sa_probe_mfma_bf16: 1024 workgroups (16 waves per CU) x 20000 rounds of four
+    32x32x16 bf16 MFMA chains, about 5 ms per launch."""
+    import ctypes
+    wgs, iters = 1024, 20000
+    buf = torch.empty(wgs * 256, dtype=torch.float32, device="cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def run():
+        if lib.sa_probe_mfma_bf16(ctypes.c_void_p(buf.data_ptr()), wgs, iters,
+                                  1 if random_operands else 0, stream):
+            raise RuntimeError("sa_probe_mfma_bf16 failed")
+    ms = time_steps(torch, run, 10, 3)
+    return round(lib.sa_probe_mfma_bf16_flops(wgs, iters) / ms / 1e9, 1)
 
 
 def gemm_probe(torch):
@@ -896,11 +911,15 @@ def main(argv=None):
             "wrapper_ms_off_on": [1.3172, 1.4298], "attention_ms_off_on": [1.1261, 1.2121],
             "prep_ms_off_on": [0.0145, 0.0176]}
         result["paths"] = paths
-        # the part's library bf16 GEMM in the same run (same lease, clocks and thermals), as a
-        # reference point for the headline's rate; not part of the roofline
+        # the part's library bf16 GEMM and its matrix-core rate on random operands in the same
+        # run (same lease, clocks and thermals), as reference points for the headline's rate; not
+        # part of the roofline, which uses the published peak
         gemm = gemm_probe(torch)
+        mfma = mfma_probe(torch, probe_lib(), True)
         result["same_run_reference"] = {"hipblaslt_bf16_gemm_8192_tflops": gemm,
-                                        "headline_over_gemm": round(tflops / gemm, 3)}
+                                        "headline_over_gemm": round(tflops / gemm, 3),
+                                        "mfma_bf16_random_operands_tflops": mfma,
+                                        "headline_over_mfma": round(tflops / mfma, 3)}
     if not args.no_cpu_baseline and not only:
         result["cpu_baseline"] = cpu_baseline(q, k, v, wl, lam, P, args.cpu_seconds)
     print(json.dumps(result))
