@@ -167,11 +167,38 @@ __device__ __forceinline__ void mask_rows(f32x16& s, int kb, int lim) {
 // out of the 32 KB L1 between them (measured on 16 x 8 KV heads x 8192 keys: 63.4 us per pass that
 // way, 56.5 us through LDS).  Scores go to the workspace head-major and in key order,
 // [GM][nKT*block_k] per (batch, KV head).
+//
+// The K copies carry the non-temporal hint (nt): the key stream is read once, and without the hint
+// it runs through L2 and evicts the score lines the stores leave there, which then go out to HBM in
+// the middle of the read stream.  With it the scores stay in L2 for decode_attend, and both
+// kernels run near the part's read rate (16 x 8 KV heads x 8192 keys: 57.0 -> 52.8 us for this
+// kernel and 55.6 -> 45.9 us for decode_attend).  The hint only suits streams read once: the
+// prefill kernels re-read every K/V tile from L2 for many query tiles.
+template <class L>
+__device__ __forceinline__ void copy_k_stream(char* lds, const __bf16* base, int bytes,
+                                              int stride_b, int lane_off) {
+  const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, max(0, bytes),
+                                                      0x00020000);
+  int sb = stride_b;
+  asm volatile("" : "+s"(sb));   // keep the block offsets out of SGPRs across the loop
+#pragma unroll
+  for (int blk = 0; blk < L::kBlocks; ++blk) {
+    const int voff = lane_off + blk * L::kRowShiftPerBlock * sb;
+    const unsigned dst = lds0 + blk * L::kPitch;
+    // as Dma::copy (M0 = LDS destination, rows past `bytes` arrive as zeros), plus nt
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :
+                 : "s"(dst), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+  }
+}
+
 template <int D, int GM, int CPT>
 __global__ __launch_bounds__(kDecThreads) void decode_scores(DecodeArgs a) {
   constexpr int KS = D / 16;   // MFMA k-steps per key block
   using L = KLayout<D>;
-  using DmaK = Dma<L, 1>;      // one wave copies a whole chunk
+  using DmaK = Dma<L, 1>;      // lane offsets of a one-wave copy of a whole chunk
   const AttnGeom& g = a.g;
   const DecUnit u = dec_unit(a);
   const int lane = threadIdx.x & 63;
@@ -218,7 +245,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_scores(DecodeArgs a) {
     const int key0 = chunk_key0(q);
     const int rows = min(u.len - key0, 64);
     const int bytes = rows > 0 ? (rows - 1) * kstride_b + D * 2 : 0;
-    DmaK::copy(kbuf[wave][q & 1], kslab + (int64_t)key0 * g.ks[1], bytes, kstride_b, lo, 0);
+    copy_k_stream<L>(kbuf[wave][q & 1], kslab + (int64_t)key0 * g.ks[1], bytes, kstride_b, lo.off);
   };
   float mx = -INFINITY;     // running max of this lane's keys in the current tile (its head)
   float tile_m = -INFINITY; // the last finished tile's max of head col, in the log2 domain
