@@ -235,6 +235,8 @@ __device__ __forceinline__ void softmax_pv(const Pol& pol, int step, const f32x1
 //   bool negligible(const float (&M)[QB], const float (&mt)[QB], int lane) const;   [kDecide]
 //   bool visible(int step) const;   the step holds an unmasked key of this wave's rows [kDecide]
 //   void filter(int step, f32x16 (&s)[2][QB], int lane) const;  dropped keys -> -inf   [kFilter]
+//   bool exports() const;  the filter's debug exports are on: filter every visited step
+//                                                                   [kFilter and kDecide]
 //   bool weighted(int step) const; float weight(int step, int kb, int r, int lane) const; [kWeighted]
 //   void record(int tile, bool keep, const float (&M)[QB], int wave, int lane, bool leader);
 // On return o, mref and l hold the unnormalised accumulator, exponent reference and row-sum
@@ -282,13 +284,15 @@ struct Mainloop {
     DmaV::copy(sm.v[step & 1], t.v, t.v_bytes, t.v_stride_b, vlo, wave);
   }
 
-  // S(step) from the K tile in LDS, masked, with its row maxima; a filtering policy (N:M) then
-  // sets the scores of the keys it drops to -inf.
+  // S(step) from the K tile in LDS, masked, with its row maxima; without decisions a filtering
+  // policy (N:M) then sets the scores of the keys it drops to -inf.  With decisions the filter runs
+  // once the step is decided, on kept steps only (the tile maxima it leaves unchanged are already
+  // taken: the rule keeps every group maximum).
   __device__ __forceinline__ void scores(int step, f32x16 (&s)[2][QB], TS& ts) {
     qk_tile<D, QB>(sm.k[step & 1], qf, s, lane);
     pol.mask(step, s, lane);
     tile_row_max<QB>(s, c32, ts.M);
-    if constexpr (Pol::kFilter) pol.filter(step, s, lane);
+    if constexpr (Pol::kFilter && !Pol::kDecide) pol.filter(step, s, lane);
   }
 
   // Each wave publishes "some row of this tile is not negligible" in LDS (for the second half of a
@@ -376,7 +380,11 @@ struct Mainloop {
         lds_barrier();
       }
     }
-    // 4: softmax(j) fused with O += P(j) V(j)
+    // 4: the filter of a kept step j (of every step while the filter's exports are on), then
+    // softmax(j) fused with O += P(j) V(j)
+    if constexpr (Pol::kFilter) {
+      if (ta.keep || pol.exports()) pol.filter(j, sa, lane);
+    }
     if (ta.keep) softmax_pv<D, QB>(pol, j, sa, ta, mref, l, o, sm.v[j & 1], c32, lane);
     // 5: S(j+2) into sa, its row maxima and votes (mt already holds every kept tile up to j+1)
     if (j + 2 < n) {

@@ -590,7 +590,8 @@ struct NmPolicy : KeyTiles<QB> {
 };
 
 // Both rules: the skip decision on the tile maxima (equal to the maxima over the N:M-kept keys),
-// the N:M bits inside every kept tile.
+// the N:M bits inside every kept tile (a skipped tile needs none: the filter runs after the
+// decision, on kept tiles).
 template <int D, int NW, int QB, int M, bool kPair = false>
 struct SkipNmPolicy : SkipDecision<D, NW, QB, false, kPair> {
   using Skip = SkipDecision<D, NW, QB, false, kPair>;
@@ -603,6 +604,10 @@ struct SkipNmPolicy : SkipDecision<D, NW, QB, false, kPair> {
   }
   __device__ __forceinline__ void filter(int j, f32x16 (&s)[2][QB], int lane) const {
     nm.filter(*this, j, s, lane);
+  }
+  // the raw scores or keep bits are exported: every visited tile is filtered, kept or not
+  __device__ __forceinline__ bool exports() const {
+    return nm.scores != nullptr || nm.keep_bits != nullptr;
   }
   __device__ __forceinline__ void finish(const SkipNmArgs& a, const TileUnit& u, int tid) const {
     Skip::finish(a, u, tid);
