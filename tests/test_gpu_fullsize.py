@@ -254,6 +254,18 @@ def test_skip_nm_full_size(target):
                        recent=recent)
     del rm, sc
 
+    # the launch the benchmark times: no debug exports, so the N:M filter runs on kept tiles only;
+    # its decisions and outputs are those of the exporting run, bit for bit
+    o_run = torch.empty_like(qd)
+    st_run = torch.full_like(st, 255)
+    lse_run = torch.empty_like(lse)
+    sa.sa_skip_nm_softmax_fwd(qd, kd, vd, o_run, lam, 2, 4, sink, recent, causal=True,
+                              block_q=Br, block_k=Bc, tile_state=st_run, lse=lse_run)
+    torch.cuda.synchronize()
+    assert np.array_equal(st_run.cpu().numpy(), state)
+    assert torch.equal(o_run.view(torch.int16), o.view(torch.int16))
+    assert torch.equal(lse_run, lse)
+
     units = sample_units(B * Hq * nQT, wl.seed + 77)
     keep_all = bits.cpu().numpy().view(np.uint32)
     kw = dict(causal=True, block_q=Br, block_k=Bc, scale=wl.scale, lam=lam, n=2, m=4, sink=sink,
@@ -265,9 +277,9 @@ def test_skip_nm_full_size(target):
     assert (st_i[vis] == flat[vis]).mean() >= 0.999
     o_ref, lse_ref, _, _, _ = oracle.skip_nm_softmax(q, k, v, mode=2, state_in=state,
                                                      keep_in=keep_all, **kw)
-    got = o_rows(from_dev_bf16(o), units, Hq, nQT, Br, Sq)
+    got = o_rows(from_dev_bf16(o_run), units, Hq, nQT, Br, Sq)
     assert_output_parity(got[valid], o_ref[valid], "skip + 2:4 O")
-    lse_got = lse_rows(lse.cpu().numpy(), units, Hq, nQT, Br, Sq)
+    lse_got = lse_rows(lse_run.cpu().numpy(), units, Hq, nQT, Br, Sq)
     assert err(lse_got[valid], lse_ref[valid])[0] < 2e-3
 
 

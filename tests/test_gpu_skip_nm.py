@@ -9,7 +9,9 @@ For every case the GPU runs with all exports on, then:
     equal the GPU's bit for bit;
   * independent: the oracle's float64 tile decisions agree on >= 99.9 % of visited tiles;
   * output: the oracle, forced onto the GPU's tile states and keep bits, matches O within max-abs
-    2e-2 / mean-abs 2e-3 and the LSE within 2e-3; counters equal the tile_state histogram.
+    2e-2 / mean-abs 2e-3 and the LSE within 2e-3; counters equal the tile_state histogram;
+  * the same call without the debug exports (the N:M filter then runs on kept tiles only) gives
+    the same tile states and matches the same oracle output.
 """
 import math
 
@@ -55,6 +57,20 @@ def run_gpu(q, k, v, causal, Br, lam, n, m, sink, recent, Bc=64):
                 st_skip=st_skip.cpu().numpy(), bits_nm=bits_nm.cpu().numpy().view(np.uint32))
 
 
+def run_gpu_plain(q, k, v, causal, Br, lam, n, m, sink, recent, Bc=64):
+    """The combined kernel with no debug exports: O, tile states and LSE only."""
+    B, Sq, Hq, D = q.shape
+    nQT, nKT = -(-Sq // Br), -(-k.shape[1] // Bc)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o = torch.full((B, Sq, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    st = torch.full((B, Hq, nQT, nKT), 255, dtype=torch.uint8, device="cuda")
+    lse = torch.full((B, Hq, Sq), float("nan"), device="cuda")
+    sa.sa_skip_nm_softmax_fwd(qd, kd, vd, o, lam, n, m, sink, recent, causal=causal, block_q=Br,
+                              block_k=Bc, tile_state=st, lse=lse)
+    torch.cuda.synchronize()
+    return from_dev_bf16(o), st.cpu().numpy(), lse.cpu().numpy()
+
+
 def check(q, k, v, causal, Br, lam, n, m, sink, recent, tag, Bc=64):
     announce(f"skip+nm {tag} lam={lam} {n}:{m} sink={sink} recent={recent} Bc={Bc}")
     D = q.shape[-1]
@@ -80,6 +96,13 @@ def check(q, k, v, causal, Br, lam, n, m, sink, recent, tag, Bc=64):
     assert_output_parity(g["o"], o_ref, tag)
     lmx, _ = err(g["lse"], lse_ref)
     assert lmx < 2e-3, f"lse {lmx}"
+    # without the debug exports the N:M filter runs on kept tiles only (the production launch):
+    # the same decisions, and the oracle's output on them
+    o2, st2, lse2 = run_gpu_plain(q, k, v, causal, Br, lam, n, m, sink, recent, Bc)
+    assert np.array_equal(st2, st), "tile states differ without the exports"
+    assert_output_parity(o2, o_ref, tag + " (no exports)")
+    lmx, _ = err(lse2, lse_ref)
+    assert lmx < 2e-3, f"lse without exports {lmx}"
     return st
 
 
