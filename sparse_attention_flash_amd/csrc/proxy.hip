@@ -240,15 +240,18 @@ void proxy_kernel(ProxyArgs a) {
 // each with its own double-buffered K/V tiles (2 x 68 KB of LDS, one workgroup per CU).  Waves 0-3
 // compute (two per query block) and waves 4-7 only copy (two per query block); waves w and w + 4
 // share a SIMD, so every SIMD holds one compute wave and one copy wave.  Both blocks advance in
-// lockstep through one barrier per step; the block with fewer exact tiles idles at the end.
+// lockstep through two barriers per step; the block with fewer exact tiles idles at the end.
 //
-//   copy waves:    K(0), V(0), K(1); wait K(0); barrier 0;
-//                  step j: wait V(j), K(j+1); barrier j+1; request V(j+1), K(j+2)
-//   compute waves: barrier 0; S(0);
-//                  step j: barrier j+1; softmax(j) + O += P(j) V(j); S(j+1)
-// At barrier j+1 the compute waves are done with V(j-1) and K(j), the buffers the copies that
-// follow it overwrite.  The summary tiles (proxy on) follow in a loop of their own, double-buffered
-// the same way with one barrier per tile.
+//   copy waves:    K(0), V(0), K(1), V(1); wait K(0); barrier;
+//                  step j: wait V(j), K(j+1); barrier A(j); request K(j+2);
+//                          barrier B(j); request V(j+2)
+//   compute waves: barrier; S(0);
+//                  step j: barrier A(j); softmax(j) + O += P(j) V(j); barrier B(j); S(j+1)
+// At A(j) the compute waves are done with K(j) (S(j) ran before it), at B(j) with V(j): each
+// buffer is refilled as soon as it is free, so every copy has about one and a half steps to land.
+// (With one barrier per step, V(j+1) was requested only at the start of step j and arrived late:
+// the kernel waited on its copies.)  The summary tiles (proxy on) follow in a loop of the same
+// shape.
 constexpr int kPcGroups = 2;   // query blocks per workgroup
 constexpr int kPcWaves = 2;    // compute (and copy) waves per query block
 
@@ -325,44 +328,54 @@ void proxy_pc_kernel(ProxyArgs a) {
     }
     if (n > 1) {
       issue_k(1);
-      wait_vmcnt<2 * kN>();   // K(0) landed
+      issue_v(1);
+      wait_vmcnt<3 * kN>();   // K(0) landed
     } else {
       wait_vmcnt<kN>();
     }
     lds_barrier();
     for (int j = 0; j < N; ++j) {
-      wait_vmcnt<0>();   // V(j), K(j+1)
-      lds_barrier();
-      if (j + 1 < n) issue_v(j + 1);
+      // V(j) and K(j+1) landed; V(j+1), requested after K(j+1), may still be in flight
+      if (j + 1 < n) wait_vmcnt<kN>(); else wait_vmcnt<0>();
+      lds_barrier();   // A(j): S(j) is done, K(j)'s buffer is free
       if (j + 2 < n) issue_k(j + 2);
+      lds_barrier();   // B(j): P.V(j) is done, V(j)'s buffer is free
+      if (j + 2 < n) issue_v(j + 2);
     }
     if (n_sum > 0) {
       // summary tile t (64 rows of k_mean / v_sum) into buffer t&1
       const int64_t sbase = ((int64_t)b * g.Hkv + hk) * nKB * D;
       const auto sklo = DmaK::lane_offsets(D * 2, rank, lane);
       const auto svlo = DmaV::lane_offsets(D * 2, rank, lane);
-      auto issue_s = [&](int t) {
-        if (!present) return;
+      // rows past nKB read as zeros (and are masked); a missing query block copies nothing
+      auto issue_sk = [&](int t) {
         const int r0 = t * kKeysPerTile;
-        const int bytes = (nKB - r0) * D * 2;   // rows past nKB read as zeros (and are masked)
-        DmaK::copy(sm.k[t & 1], (const __bf16*)a.k_mean + sbase + (int64_t)r0 * D, bytes, D * 2,
-                   sklo, rank);
-        DmaV::copy(sm.v[t & 1], (const __bf16*)a.v_sum + sbase + (int64_t)r0 * D, bytes, D * 2,
-                   svlo, rank);
+        DmaK::copy(sm.k[t & 1], (const __bf16*)a.k_mean + sbase + (int64_t)r0 * D,
+                   present ? (nKB - r0) * D * 2 : 0, D * 2, sklo, rank);
+      };
+      auto issue_sv = [&](int t) {
+        const int r0 = t * kKeysPerTile;
+        DmaV::copy(sm.v[t & 1], (const __bf16*)a.v_sum + sbase + (int64_t)r0 * D,
+                   present ? (nKB - r0) * D * 2 : 0, D * 2, svlo, rank);
       };
       lds_barrier();   // the compute waves are done with every exact tile
-      issue_s(0);
+      issue_sk(0);
+      issue_sv(0);
       if (n_sum > 1) {
-        issue_s(1);
-        wait_vmcnt<2 * kN>();   // tile 0 landed
+        issue_sk(1);
+        issue_sv(1);
+        wait_vmcnt<3 * kN>();   // K(0) landed
       } else {
-        wait_vmcnt<0>();
+        wait_vmcnt<kN>();
       }
       lds_barrier();
-      for (int t = 1; t < n_sum; ++t) {
-        wait_vmcnt<0>();   // tile t
-        lds_barrier();     // the compute waves are done with tile t-1
-        if (t + 1 < n_sum) issue_s(t + 1);
+      // the exact loop's schedule over the summary tiles
+      for (int t = 0; t < n_sum; ++t) {
+        if (t + 1 < n_sum) wait_vmcnt<kN>(); else wait_vmcnt<0>();
+        lds_barrier();   // A(t)
+        if (t + 2 < n_sum) issue_sk(t + 2);
+        lds_barrier();   // B(t)
+        if (t + 2 < n_sum) issue_sv(t + 2);
       }
     }
     return;
@@ -390,24 +403,29 @@ void proxy_pc_kernel(ProxyArgs a) {
   lds_barrier();
   if (n > 0) scores(0);
   for (int j = 0; j < N; ++j) {
-    lds_barrier();
+    lds_barrier();   // A(j)
     if (j < n) softmax_pv<D, QB>(pol, j, s, ts, mref, l, o, sm.v[j & 1], g.c32, lane);
+    lds_barrier();   // B(j)
     if (j + 1 < n) scores(j + 1);
   }
 
   if (n_sum > 0) {
     SummaryPolicy<QB> sp;
     sp.init(a, route_row, nKB, h);
-    lds_barrier();
+    auto summary_scores = [&](int t) {
+      qk_tile<D, QB>(sm.k[t & 1], qf, s, lane);
+      sp.mask(t, s);
+      tile_row_max<QB>(s, g.c32, ts.M);
+      ts.keep = true;
+    };
+    lds_barrier();   // every exact tile is done
+    lds_barrier();   // summary K(0) has landed
+    if (present) summary_scores(0);
     for (int t = 0; t < n_sum; ++t) {
-      lds_barrier();   // summary tile t has landed
-      if (present) {
-        qk_tile<D, QB>(sm.k[t & 1], qf, s, lane);
-        sp.mask(t, s);
-        tile_row_max<QB>(s, g.c32, ts.M);
-        ts.keep = true;
-        softmax_pv<D, QB>(sp, t, s, ts, mref, l, o, sm.v[t & 1], g.c32, lane);
-      }
+      lds_barrier();   // A(t)
+      if (present) softmax_pv<D, QB>(sp, t, s, ts, mref, l, o, sm.v[t & 1], g.c32, lane);
+      lds_barrier();   // B(t)
+      if (present && t + 1 < n_sum) summary_scores(t + 1);
     }
   }
   if (!present) return;
