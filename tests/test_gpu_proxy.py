@@ -139,7 +139,7 @@ def test_proxy_parity(cfg, use_proxy):
 @pytest.mark.parametrize("D", [64, 128])
 def test_proxy_uneven_routes(D, use_proxy):
     """64-row query blocks run two to a workgroup in lockstep: rows of very different exact-block
-    counts (none, a few, all) side by side, and an odd number of query blocks."""
+    counts (none, one, two, a few, all) side by side, and an odd number of query blocks."""
     B, S, H, Bq, Bk = 1, 1100, 2, 64, 64
     announce(f"proxy uneven routes D={D} use_proxy={use_proxy}")
     q, k, v = W.gen_iid(56, B, S, S, H, H, D)
@@ -149,8 +149,8 @@ def test_proxy_uneven_routes(D, use_proxy):
     for hh in range(H):
         for qb in range(nQB):
             kind = (qb + hh) % 4
-            if kind == 1:
-                bits[0, hh, qb, rng.choice(nKB, 2, replace=False)] = True
+            if kind == 1:   # one or two exact blocks: the shortest step counts
+                bits[0, hh, qb, rng.choice(nKB, 1 + (qb // 4) % 2, replace=False)] = True
             elif kind == 2:
                 bits[0, hh, qb] = True
             elif kind == 3:
