@@ -191,6 +191,26 @@ def test_proxy_off_is_exact_blocks_only(S):
     assert np.abs(lse - refs.lse(q, k, 1 / math.sqrt(32), mask)).max() < 1e-12
 
 
+def test_proxy_off_never_reads_the_summaries():
+    # "Description": omitted blocks are approximated only when the proxy is on.  With it off the
+    # output is the exact blocks' attention whatever the summaries hold -- here summaries whose
+    # logits would dwarf every exact score, so using them anywhere (even for the reference max)
+    # changes the result.
+    S, Bq, Bk = 200, 64, 64
+    q, k, v = W.gen_iid(48, 1, S, S, 2, 2, 32)
+    nQB, nKB = -(-S // Bq), -(-S // Bk)
+    bm = W.gen_bitmask(48, 1, 2, nQB, nKB, 2, garbage_padding=True)
+    km, vs = W.block_summaries(k, v, Bk)
+    qsum = refs.f64(q).sum(axis=(0, 1, 2))            # a direction every query leans along
+    huge = np.broadcast_to(np.sign(qsum) * 2000.0, km.shape)
+    km_big = W.to_bf16_bits(huge)
+    vs_big = W.to_bf16_bits(np.full(vs.shape, 1000.0))
+    o_a, lse_a = _proxy(q, k, v, bm, Bq, Bk, 0, km, vs)
+    o_b, lse_b = _proxy(q, k, v, bm, Bq, Bk, 0, km_big, vs_big)
+    assert np.array_equal(o_a, o_b) and np.array_equal(lse_a, lse_b)
+    assert np.isfinite(lse_a).all()
+
+
 def test_proxy_changes_output_and_padding_is_ignored():
     S, Bq, Bk = 257, 64, 64
     q, k, v = W.gen_iid(48, 1, S, S, 1, 1, 32)
