@@ -230,6 +230,19 @@ def test_forced_mode_follows_given_states():
     assert np.abs(o - refs.sdpa(q, k, v, 0.25, mask=mask)).max() < 1e-12
 
 
+def test_forced_mode_with_every_tile_skipped_is_empty():
+    # A row that attends to nothing has O = 0 and LSE = log 0 = -inf (the convention every path
+    # shares); only forced states can produce it, since a free run always keeps a row's first
+    # tile.  Rows past Sq keep LSE 0 (they are padding, not rows).
+    q, k, v = W.gen_iid(27, 1, 100, 128, 1, 1, 16)
+    st_in = np.ones((1, 1, 2, 2), np.uint8)
+    o, lse, st, _ = _run(q, k, v, False, 64, 64, 0.0, mode=2, state_in=st_in)
+    assert (st == 1).all() and (o == 0).all()
+    assert np.isneginf(lse).all()
+    ou, lu, _, _ = _run(q, k, v, False, 64, 64, 0.0, mode=2, state_in=st_in, units=[1])
+    assert np.isneginf(lu[0, :36]).all() and (lu[0, 36:] == 0).all()
+
+
 def test_units_subset_matches_full_run():
     q, k, v = W.gen_llm(26, 1, 256, 4, 2, 32)
     o, lse, st, rm = _run(q, k, v, True, 64, 64, 0.9)
